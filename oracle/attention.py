@@ -1,0 +1,123 @@
+"""Exact attention, written as its plain definition, in float64 (test infrastructure only).
+
+What is computed (Day-21 page §3.1 "standard implementation data flow" and §5.1;
+M4-047 card §3):
+    S   = scale * Q K^T                       (Nq x Nk; scale = 1/sqrt(d) in the pages)
+    S_ij = -inf where j > i                   (causal mask, only when requested)
+    m_i = max_j S_ij                          (pass 1 of the safe softmax, Day-21 §5.1)
+    e_ij = exp(S_ij - m_i), l_i = sum_j e_ij  (pass 2)
+    P   = e / l,  O = P V
+    LSE_i = m_i + ln(l_i)                     (the per-row statistic kept for the backward
+                                               recompute, M4-047 card §3 point (c))
+
+Rows may be processed in chunks to bound memory, but every chunk spans all keys,
+so each row's two passes see the whole row.  Nothing here uses the online recurrence.
+
+Split-KV decode (Q31 answer, follow-up 3: split K/V into chunks processed in parallel,
+then merge; the merge rescales with exp(m_block - m_global), follow-up 2):
+    split_partials  per split s over keys [a_s, b_s): m_s, l_s = sum exp(S - m_s),
+                    O_s = sum_j exp(S_j - m_s) v_j (unnormalised)
+    combine_partials M = max_s m_s, w_s = exp(m_s - M), L = sum w_s l_s,
+                    O = sum w_s O_s / L, LSE = M + ln L; an empty split (m_s = -inf,
+                    l_s = 0) has weight 0.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def scores(q, k, scale: float, causal: bool, row_offset: int = 0) -> np.ndarray:
+    """S = scale * q k^T for query rows row_offset.. (+ causal -inf above the diagonal)."""
+    s = float(scale) * (_f64(q) @ _f64(k).T)
+    if causal:
+        i = np.arange(s.shape[0])[:, None] + row_offset
+        j = np.arange(s.shape[1])[None, :]
+        s = np.where(j > i, -np.inf, s)
+    return s
+
+
+def softmax_two_pass(s: np.ndarray):
+    """Row-wise safe softmax in two passes: returns (P, m, l)."""
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return e / l, m[..., 0], l[..., 0]
+
+
+def attention_head(q, k, v, scale: float, causal: bool = False, rows=None, row_chunk: int = 1024):
+    """One head. q [Nq, d], k and v [Nk, d] -> (O [n, d], LSE [n]) in float64.
+
+    rows: optional increasing 1-D array of query row indices to compute (the causal
+    mask uses the true row index); default all rows.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    o = np.empty((len(rows), v.shape[1]), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
+    for c0 in range(0, len(rows), row_chunk):
+        r = rows[c0:c0 + row_chunk]
+        s = float(scale) * (q[r] @ k.T)
+        if causal:
+            s = np.where(np.arange(k.shape[0])[None, :] > r[:, None], -np.inf, s)
+        p, m, l = softmax_two_pass(s)
+        o[c0:c0 + len(r)] = p @ v
+        lse[c0:c0 + len(r)] = m + np.log(l)
+    return o, lse
+
+
+def attention(q, k, v, scale: float, causal: bool = False, row_chunk: int = 1024):
+    """[B, H, Nq, d] x [B, H, Nk, d] x [B, H, Nk, d] -> (O [B, H, Nq, d], LSE [B, H, Nq]) float64."""
+    q = np.asarray(q)
+    B, H, Nq, _ = q.shape
+    o = np.empty(q.shape[:3] + (np.asarray(v).shape[-1],), dtype=np.float64)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], scale, causal,
+                                                row_chunk=row_chunk)
+    return o, lse
+
+
+def attention_probs(q, k, scale: float, causal: bool = False) -> np.ndarray:
+    """The full probability matrix P of one head (small inputs only)."""
+    p, _, _ = softmax_two_pass(scores(q, k, scale, causal))
+    return p
+
+
+def split_bounds(nk: int, num_splits: int):
+    """Contiguous splits of ceil(nk / num_splits) keys; trailing splits may be short or empty."""
+    chunk = -(-nk // num_splits)
+    return [(min(nk, s * chunk), min(nk, (s + 1) * chunk)) for s in range(num_splits)]
+
+
+def split_partials(q, k, v, scale: float, num_splits: int):
+    """One query q [d] against k, v [Nk, d]: per-split (O_s [S, d], m_s [S], l_s [S])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S = num_splits
+    o = np.zeros((S, v.shape[1]), dtype=np.float64)
+    m = np.full(S, -np.inf, dtype=np.float64)
+    l = np.zeros(S, dtype=np.float64)
+    for s, (a, b) in enumerate(split_bounds(k.shape[0], S)):
+        if b <= a:
+            continue  # empty split: m = -inf, l = 0, O = 0
+        x = float(scale) * (k[a:b] @ q)
+        m[s] = x.max()
+        e = np.exp(x - m[s])
+        l[s] = e.sum()
+        o[s] = e @ v[a:b]
+    return o, m, l
+
+
+def combine_partials(o_s, m_s, l_s):
+    """Merge split partials: (O [d], LSE) in float64."""
+    o_s, m_s, l_s = _f64(o_s), _f64(m_s), _f64(l_s)
+    M = m_s.max()
+    w = np.where(np.isneginf(m_s), 0.0, np.exp(m_s - M))
+    L = float((w * l_s).sum())
+    return (w @ o_s) / L, M + math.log(L)
