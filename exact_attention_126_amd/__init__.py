@@ -1,1 +1,161 @@
-"""MI355X exact attention: fused forward and split-KV decode (binding added with the library)."""
+"""MI355X exact attention: Python binding of the C ABI in include/fa.h.
+
+The functions below only marshal arguments (torch tensors -> device pointers, sizes, the
+current HIP stream) and call libfa.so; every step of the computation runs in the library's
+HIP kernels.  There is no fallback: if the library is missing, calls raise.
+
+torch is imported before libfa.so is loaded so that the process maps a single HIP runtime
+(torch's) and torch's streams are valid inside the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_DTYPE_BF16 = 0
+FA_DTYPE_F32 = 1
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE", 4: "FA_ERR_UNSUPPORTED",
+                5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
+EXPORTED = ["fa_fwd", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_combine", "fa_status_string"]
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({fa_status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_attention_126_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, vp]
+        L.fa_fwd.restype = i32
+        L.fa_decode_workspace_bytes.argtypes = [i64, i64, i64, i32]
+        L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_decode_split.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, f32, i32, i32, vp]
+        L.fa_decode_split.restype = i32
+        L.fa_decode_combine.argtypes = [vp, ctypes.c_size_t, vp, vp, i64, i64, i64, i32, i32, vp]
+        L.fa_decode_combine.restype = i32
+        L.fa_status_string.argtypes = [i32]
+        L.fa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _raise(status: int, where: str):
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+def fa_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = None, stream=None) -> None:
+    """Fused attention forward into caller-provided o [B,H,Nq,d] and lse [B,H,Nq] (float32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, n, q.dtype)
+    _check(lse, "lse", torch.float32)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)),
+                      float(scale), _dtype_code(q), _stream(stream))
+    _raise(st, "fa_fwd")
+
+
+def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def fa_decode_split(q, k, v, workspace, num_splits: int, scale: float | None = None, stream=None) -> None:
+    """Per-split partials of one-token decode; q [B,H,1,d], k/v [B,H,Nk,d], workspace uint8/float32."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    _check(workspace, "workspace")
+    B, H, _, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               B, H, Nk, d, float(scale), int(num_splits), _dtype_code(q), _stream(stream))
+    _raise(st, "fa_decode_split")
+
+
+def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None) -> None:
+    """Merge the split partials into o [B,H,1,d] and lse [B,H,1]."""
+    _check(workspace, "workspace")
+    _check(o, "o")
+    _check(lse, "lse", torch.float32)
+    B, H, _, d = o.shape
+    st = lib().fa_decode_combine(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(o), _ptr(lse),
+                                 B, H, d, int(num_splits), _dtype_code(o), _stream(stream))
+    _raise(st, "fa_decode_combine")
+
+
+# ---- conveniences that allocate the outputs with torch and call the entry points above
+def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """(o, lse) = attention(q, k, v): allocates the outputs and calls fa_fwd."""
+    B, H, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def decode_workspace(q, num_splits: int):
+    B, H, _, d = q.shape
+    return torch.empty(fa_decode_workspace_bytes(B, H, d, num_splits) // 4, dtype=torch.float32, device=q.device)
+
+
+def decode(q, k, v, num_splits: int, scale: float | None = None, workspace=None, stream=None):
+    """(o, lse) of one-token decode: fa_decode_split then fa_decode_combine on the same stream."""
+    B, H, _, d = q.shape
+    if workspace is None:
+        workspace = decode_workspace(q, num_splits)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    fa_decode_split(q, k, v, workspace, num_splits, scale, stream)
+    fa_decode_combine(workspace, o, lse, num_splits, stream)
+    return o, lse

@@ -1,0 +1,99 @@
+// C ABI of the attention library: host-side validation, then dispatch to the kernel files.
+// Every check runs before any HIP call, so invalid arguments never reach the GPU.
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool dtype_ok(fa_dtype_t t) { return t == FA_DTYPE_BF16 || t == FA_DTYPE_F32; }
+int64_t elt_bytes(fa_dtype_t t) { return t == FA_DTYPE_BF16 ? 2 : 4; }
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+// One head's tensor must be addressable with 32-bit byte offsets.
+bool head_fits(int64_t n, int64_t d, fa_dtype_t t) { return n <= kI32Max / (d * elt_bytes(t)); }
+
+fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, fa_dtype_t dtype,
+                   hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!dtype_ok(dtype) || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (causal && Nq != Nk) return FA_ERR_SHAPE;
+  if (!head_fits(Nq, d, dtype) || !head_fits(Nk, d, dtype)) return FA_ERR_SHAPE;
+  if (B > kI32Max / H || B * H > kI32Max / ((Nq + 31) / 32)) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, (int)B, (int)H, (int)Nq, (int)Nk, (int)d, causal != 0, scale};
+  return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, stream) : fa::launch_fwd_f32(a, stream));
+}
+
+size_t fa_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int num_splits) {
+  if (B <= 0 || H <= 0 || d <= 0 || num_splits <= 0) return 0;
+  if (B > kI32Max / H || B * H > kI32Max / num_splits) return 0;
+  return (size_t)(B * H * num_splits) * (size_t)(d + 2) * sizeof(float);
+}
+
+fa_status_t fa_decode_split(const void* q, const void* k, const void* v, void* workspace, size_t workspace_bytes,
+                            int64_t B, int64_t H, int64_t Nk, int64_t d, float scale, int num_splits,
+                            fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !workspace) return FA_ERR_NULL;
+  if (!dtype_ok(dtype) || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(workspace, 16)) return FA_ERR_ALIGN;
+  if (B <= 0 || H <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (!head_fits(Nk, d, dtype) || B > kI32Max / H) return FA_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > Nk || !scale_ok(scale)) return FA_ERR_ARG;
+  if (B * H > kI32Max / num_splits) return FA_ERR_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  float* o_part = static_cast<float*>(workspace);
+  float* ml = o_part + (size_t)(B * H * num_splits) * (size_t)d;
+  fa::DecodeSplitArgs a{q, k, v, o_part, ml, (int)B, (int)H, (int)Nk, (int)d, num_splits, scale};
+  return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_decode_split_bf16(a, stream)
+                                         : fa::launch_decode_split_f32(a, stream));
+}
+
+fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse, int64_t B,
+                              int64_t H, int64_t d, int num_splits, fa_dtype_t dtype, hipStream_t stream) {
+  if (!workspace || !o || !lse) return FA_ERR_NULL;
+  if (!dtype_ok(dtype) || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(workspace, 16) || !aligned(o, 16) || !aligned(lse, 4)) return FA_ERR_ALIGN;
+  if (B <= 0 || H <= 0 || B > kI32Max / H) return FA_ERR_SHAPE;
+  if (num_splits < 1) return FA_ERR_ARG;
+  if (B * H > kI32Max / num_splits) return FA_ERR_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const float* o_part = static_cast<const float*>(workspace);
+  const float* ml = o_part + (size_t)(B * H * num_splits) * (size_t)d;
+  fa::DecodeCombineArgs a{o_part, ml, o, lse, (int)B, (int)H, (int)d, num_splits};
+  return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_decode_combine_bf16(a, stream)
+                                         : fa::launch_decode_combine_f32(a, stream));
+}
+
+const char* fa_status_string(fa_status_t s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_ALIGN: return "pointer misaligned (tensors need 16 bytes, lse 4 bytes)";
+    case FA_ERR_SHAPE: return "invalid shape (size <= 0, causal with Nq != Nk, or beyond index limits)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim (64 or 128) or dtype";
+    case FA_ERR_WORKSPACE: return "decode workspace too small";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    case FA_ERR_ARG: return "invalid scalar argument (scale must be finite and > 0; 1 <= num_splits <= Nk)";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,229 @@
+// Split-KV decode for gfx950: one query token per (batch, head) against a long KV cache.
+//
+// Decode is a matrix-vector product bound by reading the KV cache from HBM (Day-21 page
+// "GPU 学习日报 Day 21：FlashAttention：GPU Memory Hierarchy 下的 IO 优化", §9 and FAQ Q5), so
+// there is no MFMA here: the work is spread over many workgroups by splitting the keys into
+// contiguous chunks that are processed in parallel and merged afterwards (Q31 answer
+// "FlashAttention 为什么快", follow-up 3).  The merge rescales every partial result by
+// exp(m_s - max m) before summing (same answer, follow-up 2).
+//
+// decode_split_kernel: one workgroup per (batch*head, split).  D/8 (bf16) or D/4 (fp32) lanes
+// share a key row and read it with coalesced 16-byte loads; each wave walks its own keys with
+// an online softmax (running max, running sum, rescaled accumulator, Day-21 page §5.2-5.3),
+// U key rows of K and of V in flight per lane.  The four waves' states are merged through
+// LDS and written to the workspace as (O_part, m, l).
+// decode_combine_kernel: one workgroup per (batch*head), one thread per dim.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over aligned groups of W consecutive lanes (W in {8, 16, 32}); every lane gets the sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kRowHalfMirror>(x);  // pairs quad 0 with quad 1 of each 8 lanes
+  if (W >= 16) x += dpp<kRowMirror>(x);  // pairs the two 8-lane halves of each row
+  if (W >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<uint16_t> {  // bf16 storage
+  static constexpr int PER16 = 8;
+  __device__ static void widen(u32x4_t r, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(r[i] << 16);
+      f[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static uint16_t narrow(float x) { return f32_to_bf16_bits(x); }
+};
+template <>
+struct Elt<float> {
+  static constexpr int PER16 = 4;
+  __device__ static void widen(u32x4_t r, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(r[i]);
+  }
+  __device__ static float narrow(float x) { return x; }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                           const T* __restrict__ V, float* __restrict__ Opart,
+                                                           float* __restrict__ ML, int Nk, int S, int chunk,
+                                                           float sl2) {
+  constexpr int EPL = Elt<T>::PER16;  // elements per lane per key row
+  constexpr int LPK = D / EPL;        // lanes per key row
+  constexpr int KPW = 64 / LPK;       // key rows per wave per step
+  constexpr int U = 8;                // steps in flight per iteration
+  constexpr int WAVES = 4;
+  __shared__ float s_m[WAVES], s_l[WAVES];
+  __shared__ float s_acc[WAVES][D];
+
+  const int s = blockIdx.x % S;
+  const int bh = blockIdx.x / S;
+  const int start = s * chunk;
+  const int end = min(Nk, start + chunk);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int gi = lane / LPK, li = lane % LPK;
+
+  float qv[EPL];
+  Elt<T>::widen(gload16(Q + (int64_t)bh * D + li * EPL), qv);
+  const T* Kh = K + (int64_t)bh * Nk * D + li * EPL;
+  const T* Vh = V + (int64_t)bh * Nk * D + li * EPL;
+
+  float m = -INFINITY, l = 0.f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+
+  for (int base = start + wave * U * KPW; base < end; base += WAVES * U * KPW) {
+    u32x4_t kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = min(base + u * KPW + gi, end - 1);
+      kr[u] = gload16(Kh + (int64_t)key * D);
+      vr[u] = gload16(Vh + (int64_t)key * D);
+    }
+    float sc[U];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[EPL];
+      Elt<T>::widen(kr[u], kf);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
+      dot = group_sum<LPK>(dot);
+      sc[u] = (base + u * KPW + gi < end) ? dot * sl2 : -INFINITY;
+      bm = fmaxf(bm, sc[u]);
+    }
+#pragma unroll
+    for (int w = LPK; w < 64; w <<= 1) bm = fmaxf(bm, __shfl_xor(bm, w));
+    const float mnew = fmaxf(m, bm);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = fast_exp2(sc[u] - mnew);
+      float vf[EPL];
+      Elt<T>::widen(vr[u], vf);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(p, vf[e], acc[e]);
+    }
+  }
+  // fold the key groups of the wave: lanes with equal li hold the same dims
+#pragma unroll
+  for (int w = LPK; w < 64; w <<= 1) {
+    l += __shfl_xor(l, w);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], w);
+  }
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+  }
+  if (gi == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_acc[wave][li * EPL + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    float M = s_m[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, s_m[w]);
+    float o = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float f = fast_exp2(s_m[w] - M);
+        o = __builtin_fmaf(f, s_acc[w][tid], o);
+        L = __builtin_fmaf(f, s_l[w], L);
+      }
+    }
+    const int64_t rec = (int64_t)bh * S + s;
+    Opart[rec * D + tid] = o;
+    if (tid == 0) {
+      ML[rec * 2] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+      ML[rec * 2 + 1] = L;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ Opart,
+                                                             const float* __restrict__ ML, T* __restrict__ O,
+                                                             float* __restrict__ LSE, int S) {
+  const int bh = blockIdx.x;
+  const int dim = threadIdx.x;
+  const float* ml = ML + (int64_t)bh * S * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f, acc = 0.f;
+  const float* op = Opart + (int64_t)bh * S * D + dim;
+  for (int s = 0; s < S; ++s) {
+    const float f = fast_exp2((ml[2 * s] - M) * kLog2e);  // empty split: exp2(-inf) = 0
+    L = __builtin_fmaf(f, ml[2 * s + 1], L);
+    acc = __builtin_fmaf(f, op[(int64_t)s * D], acc);
+  }
+  O[(int64_t)bh * D + dim] = Elt<T>::narrow(acc / L);
+  if (dim == 0) LSE[bh] = M + fast_log2(L) * kLn2;
+}
+
+template <typename T>
+hipError_t split_impl(const DecodeSplitArgs& a, hipStream_t stream) {
+  const int chunk = (a.Nk + a.num_splits - 1) / a.num_splits;
+  const int64_t nblk = (int64_t)a.B * a.H * a.num_splits;
+  const float sl2 = a.scale * kLog2e;
+  if (a.d == 128)
+    hipLaunchKernelGGL((decode_split_kernel<T, 128>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, 64>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t combine_impl(const DecodeCombineArgs& a, hipStream_t stream) {
+  const unsigned nblk = (unsigned)((int64_t)a.B * a.H);
+  if (a.d == 128)
+    hipLaunchKernelGGL((decode_combine_kernel<T, 128>), dim3(nblk), dim3(128), 0, stream, a.o_part, a.ml, (T*)a.o,
+                       a.lse, a.num_splits);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<T, 64>), dim3(nblk), dim3(64), 0, stream, a.o_part, a.ml, (T*)a.o,
+                       a.lse, a.num_splits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_split_bf16(const DecodeSplitArgs& a, hipStream_t stream) { return split_impl<uint16_t>(a, stream); }
+hipError_t launch_decode_split_f32(const DecodeSplitArgs& a, hipStream_t stream) { return split_impl<float>(a, stream); }
+hipError_t launch_decode_combine_bf16(const DecodeCombineArgs& a, hipStream_t stream) {
+  return combine_impl<uint16_t>(a, stream);
+}
+hipError_t launch_decode_combine_f32(const DecodeCombineArgs& a, hipStream_t stream) {
+  return combine_impl<float>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,66 @@
+// Device-side helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x on the hardware transcendental unit (v_exp_f32).  exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the hardware unit (v_log_f32), x > 0 normal.
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t b = __float_as_uint(x);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two floats -> packed bf16 pair (low half = a), round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Max of a value across the two 32-lane halves of a wave (lane l and lane l ^ 32).
+__device__ __forceinline__ float max_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16-byte LDS accesses.
+__device__ __forceinline__ u32x4_t lds_load16(const FA_LDS char* p) { return *(const FA_LDS u32x4_t*)p; }
+__device__ __forceinline__ void lds_store16(FA_LDS char* p, u32x4_t v) { *(FA_LDS u32x4_t*)p = v; }
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// receives element (i % 4) of the 8-byte rows addressed by lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ i16x4_t lds_load8_tr16(const FA_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p);
+}
+
+__device__ __forceinline__ u32x4_t gload16(const void* p) { return *(const u32x4_t*)p; }
+
+}  // namespace fa

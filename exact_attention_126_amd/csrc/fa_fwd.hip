@@ -1,0 +1,432 @@
+// Fused attention forward for gfx950: O = softmax(scale * Q K^T) V and LSE per row, in one
+// kernel.  Method (Day-21 page "GPU 学习日报 Day 21：FlashAttention：GPU Memory Hierarchy 下的 IO
+// 优化", §4 tiling and §5.2-5.3 online softmax; Q31 answer "FlashAttention 为什么快", §2):
+// each workgroup owns a block of query rows and streams every K/V tile once through LDS; per
+// row it keeps a running max m, a running sum l and a rescaled output accumulator, so the
+// N x N score and probability matrices never exist outside registers.  One workgroup per
+// (batch, head, query block) is the sequence-length parallelism of the Day-21 page §6.
+//
+// gfx950 mapping (bf16 path):
+//  * Transposed products.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K tile from LDS,
+//    B = Q^T held in VGPRs for the whole kernel) puts one query per lane column: lane l holds
+//    query l % 32 and 16 of the 32 keys of an MFMA block, the other 16 sit in lane l ^ 32.
+//    Row max and row sum are then in-lane reductions plus one permlane32 swap, and the
+//    rescale factor exp2(m_old - m_new) is a per-lane scalar.
+//  * O^T = V^T P^T on the same MFMA: the S^T accumulator, converted to bf16, is directly the
+//    B operand (P^T).  To make that true, the K row each A-operand lane reads is permuted
+//    (key_of_row below) so that the 8 accumulator values lane-half h feeds to k-step t are
+//    keys 16t + 8h + 0..7 in order.
+//  * V stays in its natural [key][dim] layout in LDS and is read with the transposing
+//    ds_read_b64_tr_b16, two reads giving the 8 consecutive keys of one dim an A-operand
+//    lane needs.
+//  * LDS rows are XOR-swizzled in 16-byte chunks by the row's low four bits, chosen so that
+//    the tile stores, the K operand reads and the transposing V reads are all free of bank
+//    conflicts.
+//  * K/V tiles are double-buffered: tile t+1 is fetched into registers while tile t is
+//    consumed, and stored to the other LDS stage afterwards; one barrier per tile.
+//  * Causal: tiles wholly after a wave's last query are skipped, tiles crossing the diagonal
+//    are masked element by element (Day-21 page §6 table), and the query blocks with the
+//    most tiles are dispatched first.  Workgroups are remapped so that the ones an XCD runs
+//    together share a head's K/V in that XCD's L2.
+//  * exp is the hardware exp2 with scale * log2(e) folded into one FMA; LSE is emitted in
+//    natural-log units.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+// XOR swizzle applied to the 16-byte chunk index of an LDS row, from the row's low 4 bits.
+template <int D> struct Swz;
+template <> struct Swz<128> { static constexpr int b0 = 4, b1 = 10, b2 = 1, b3 = 3; };
+template <> struct Swz<64> { static constexpr int b0 = 2, b1 = 4, b2 = 1, b3 = 3; };
+
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return ((row & 1) ? Swz<D>::b0 : 0) ^ ((row & 2) ? Swz<D>::b1 : 0) ^
+         ((row & 4) ? Swz<D>::b2 : 0) ^ ((row & 8) ? Swz<D>::b3 : 0);
+}
+
+// The 32x32 MFMA accumulator holds row r = 8*(j/4) + 4*h + (j%4) in register j of lane-half h.
+// key_of_row(r) is the key loaded for row r so that register j of lane-half h is key
+// 16*(j/8) + 8*h + (j%8) of the 32-key block.
+__device__ __forceinline__ int key_of_row(int r) {
+  const int a = r >> 3, h = (r >> 2) & 1, b = r & 3;
+  return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+}
+
+template <int D, int QBLK>
+struct Bf16Cfg {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int BR = WAVES * 32 * QBLK;  // query rows per workgroup
+  static constexpr int BC = 64;                 // keys per tile
+  static constexpr int RB = D * 2;              // bytes per LDS row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BC * RB;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile then V tile
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int KSTEPS = D / 16;                     // MFMA k-steps of S^T = K Q^T
+  static constexpr int DBLK = D / 32;                       // 32-dim blocks of O^T
+  static constexpr int CHUNKS = TILE_BYTES / 16 / THREADS;  // 16-byte chunks per thread per tensor
+  static constexpr int ROWS_PER_PASS = THREADS / CPR;
+  static_assert(ROWS_PER_PASS % 16 == 0, "swizzle must be invariant across a thread's rows");
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int D, bool CAUSAL, int QBLK>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int xcd_remap,
+    float sl2) {
+  using C = Bf16Cfg<D, QBLK>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
+  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+
+  // ---- workgroup -> (batch*head, query block)
+  int bid = blockIdx.x;
+  if (xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  int qblk = bid % n_qblk;
+  const int bh = bid / n_qblk;
+  if (CAUSAL) qblk = n_qblk - 1 - qblk;  // most tiles first
+
+  const uint16_t* Qh = Q + (int64_t)bh * Nq * D;
+  const uint16_t* Kh = K + (int64_t)bh * Nk * D;
+  const uint16_t* Vh = V + (int64_t)bh * Nk * D;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int q_wave0 = qblk * C::BR + wave * 32 * QBLK;
+
+  // ---- Q^T fragments (B operand), resident for the whole kernel
+  bf16x8_t qf[QBLK][C::KSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < QBLK; ++qb) {
+    const int qrow = min(q_wave0 + 32 * qb + l32, Nq - 1);
+    const uint16_t* qp = Qh + (int64_t)qrow * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[qb][ks] = as_bf16x8(gload16(qp + 16 * ks));
+  }
+
+  // ---- tile range
+  const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR) : Nk;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+
+  // ---- staging: thread tid moves chunks tid + THREADS*i of each tile
+  const int st_row0 = tid / C::CPR, st_c = tid % C::CPR;
+  const int st_lds = st_row0 * C::RB + ((st_c ^ swz<D>(st_row0)) << 4);
+  u32x4_t kreg[C::CHUNKS], vreg[C::CHUNKS];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < C::CHUNKS; ++i) {
+      const int row = min(t * C::BC + st_row0 + i * C::ROWS_PER_PASS, Nk - 1);
+      kreg[i] = gload16(Kh + (int64_t)row * D + st_c * 8);
+      vreg[i] = gload16(Vh + (int64_t)row * D + st_c * 8);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    FA_LDS char* base = smem + stage * C::STAGE_BYTES + st_lds;
+#pragma unroll
+    for (int i = 0; i < C::CHUNKS; ++i) {
+      lds_store16(base + i * C::ROWS_PER_PASS * C::RB, kreg[i]);
+      lds_store16(base + C::TILE_BYTES + i * C::ROWS_PER_PASS * C::RB, vreg[i]);
+    }
+  };
+
+  // ---- per-lane LDS read offsets
+  int koff[C::KSTEPS];
+  {
+    const int krow = key_of_row(l32);
+    const int ks_sw = swz<D>(krow);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) koff[ks] = krow * C::RB + (((2 * ks + hh) ^ ks_sw) << 4);
+  }
+  int voff[C::DBLK][2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const int vh = g >> 1, ve = s >> 2, vq = s & 3;
+#pragma unroll
+    for (int mb = 0; mb < C::DBLK; ++mb)
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        const int key = 8 * vh + 4 * I + ve;
+        const int dim = 32 * mb + 16 * (g & 1) + 4 * vq;
+        voff[mb][I] = key * C::RB + (((dim >> 3) ^ swz<D>(key)) << 4) + ((dim >> 2) & 1) * 8;
+      }
+  }
+
+  f32x16_t oacc[QBLK][C::DBLK];
+  float m2[QBLK], lsum[QBLK];
+#pragma unroll
+  for (int qb = 0; qb < QBLK; ++qb) {
+    m2[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < C::DBLK; ++mb) oacc[qb][mb] = f32x16_t{};
+  }
+
+  auto tile_compute = [&](auto mask_tag, const FA_LDS char* kt, const FA_LDS char* vt, int tile0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // S^T = K Q^T for the two 32-key blocks of the tile
+    f32x16_t sacc[QBLK][2];
+#pragma unroll
+    for (int qb = 0; qb < QBLK; ++qb) sacc[qb][0] = sacc[qb][1] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const bf16x8_t a0 = as_bf16x8(lds_load16(kt + koff[ks]));
+      const bf16x8_t a1 = as_bf16x8(lds_load16(kt + 32 * C::RB + koff[ks]));
+#pragma unroll
+      for (int qb = 0; qb < QBLK; ++qb) {
+        sacc[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[qb][ks], sacc[qb][0], 0, 0, 0);
+        sacc[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[qb][ks], sacc[qb][1], 0, 0, 0);
+      }
+    }
+    // online softmax (log2 domain) and P^T packing
+    u32x4_t pb[QBLK][4];
+#pragma unroll
+    for (int qb = 0; qb < QBLK; ++qb) {
+      if (MASK) {
+        const int q = q_wave0 + 32 * qb + l32;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = tile0 + 32 * kb + 16 * (j >> 3) + 8 * hh + (j & 7);
+            if (key >= Nk || (CAUSAL && key > q)) sacc[qb][kb][j] = -INFINITY;
+          }
+      }
+      float mx = sacc[qb][0][0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[qb][0][j]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[qb][1][j]);
+      mx = max_across_halves(mx);
+      const float mnew = fmaxf(m2[qb], mx * sl2);
+      const float alpha = fast_exp2(m2[qb] - mnew);
+      m2[qb] = mnew;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[qb][kb][2 * jj], sl2, -mnew));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[qb][kb][2 * jj + 1], sl2, -mnew));
+          rs += p0 + p1;
+          pb[qb][2 * kb + (jj >> 2)][jj & 3] = pack_bf16x2(p0, p1);
+        }
+      lsum[qb] = alpha * lsum[qb] + rs;
+#pragma unroll
+      for (int mb = 0; mb < C::DBLK; ++mb) oacc[qb][mb] *= alpha;
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int mb = 0; mb < C::DBLK; ++mb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const i16x4_t lo = lds_load8_tr16(vt + voff[mb][0] + t * 16 * C::RB);
+        const i16x4_t hi = lds_load8_tr16(vt + voff[mb][1] + t * 16 * C::RB);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < QBLK; ++qb)
+          oacc[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[qb][t]), oacc[qb][mb], 0, 0, 0);
+      }
+  };
+
+  // ---- main loop over K/V tiles
+  load_tile(0);
+  store_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();  // stage t&1 is complete; stage (t+1)&1 is no longer read
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const int tile0 = t * C::BC;
+    const FA_LDS char* kt = smem + (t & 1) * C::STAGE_BYTES;
+    const FA_LDS char* vt = kt + C::TILE_BYTES;
+    const bool active = !CAUSAL || tile0 <= q_wave0 + 32 * QBLK - 1;
+    if (active) {
+      const bool need_mask = (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0);
+      if (need_mask)
+        tile_compute(std::integral_constant<bool, true>{}, kt, vt, tile0);
+      else
+        tile_compute(std::integral_constant<bool, false>{}, kt, vt, tile0);
+    }
+    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+  }
+
+  // ---- epilogue: O = O_acc / l (RNE to bf16), LSE = (m + log2 l) * ln 2
+  uint16_t* Oh = O + (int64_t)bh * Nq * D;
+  float* Lh = LSE + (int64_t)bh * Nq;
+#pragma unroll
+  for (int qb = 0; qb < QBLK; ++qb) {
+    const float l = sum_across_halves(lsum[qb]);
+    const float inv = 1.f / l;
+    const int q = q_wave0 + 32 * qb + l32;
+    if (q < Nq) {
+      uint16_t* op = Oh + (int64_t)q * D + 4 * hh;
+#pragma unroll
+      for (int mb = 0; mb < C::DBLK; ++mb)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          u32x2_t w;
+          w[0] = pack_bf16x2(oacc[qb][mb][4 * jg + 0] * inv, oacc[qb][mb][4 * jg + 1] * inv);
+          w[1] = pack_bf16x2(oacc[qb][mb][4 * jg + 2] * inv, oacc[qb][mb][4 * jg + 3] * inv);
+          *(u32x2_t*)(op + 32 * mb + 8 * jg) = w;
+        }
+      if (hh == 0) Lh[q] = (m2[qb] + fast_log2(l)) * kLn2;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+// Same structure on v_mfma_f32_32x32x2_f32 (no down-conversion anywhere).  k-steps of
+// S^T = K Q^T use the dim order k(t, h) = h*D/2 + t, so each lane reads contiguous float4s;
+// the P V product takes one accumulator register per k-step, whose key is the accumulator
+// row of that register, so no key permutation is needed.  LDS rows are padded by 16 bytes.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                      const float* __restrict__ V, float* __restrict__ O,
+                                                      float* __restrict__ LSE, int Nq, int Nk, int n_qblk,
+                                                      float sl2) {
+  constexpr int BR = 128, BC = 32, RS = D + 4, HALF = D / 2, DBLK = D / 32;
+  constexpr int TILE_FLOATS = BC * RS;
+  constexpr int CH_PER_ROW = D / 4;
+  constexpr int CHUNKS = BC * CH_PER_ROW / 256;
+  __shared__ __attribute__((aligned(16))) float kt[TILE_FLOATS];
+  __shared__ __attribute__((aligned(16))) float vt[TILE_FLOATS];
+
+  int qblk = blockIdx.x % n_qblk;
+  const int bh = blockIdx.x / n_qblk;
+  if (CAUSAL) qblk = n_qblk - 1 - qblk;
+  const float* Qh = Q + (int64_t)bh * Nq * D;
+  const float* Kh = K + (int64_t)bh * Nk * D;
+  const float* Vh = V + (int64_t)bh * Nk * D;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int q_wave0 = qblk * BR + wave * 32;
+
+  float qf[HALF];
+  {
+    const float* qp = Qh + (int64_t)min(q_wave0 + l32, Nq - 1) * D + hh * HALF;
+#pragma unroll
+    for (int i = 0; i < HALF; i += 4) {
+      const f32x4_t x = *(const f32x4_t*)(qp + i);
+      qf[i] = x[0]; qf[i + 1] = x[1]; qf[i + 2] = x[2]; qf[i + 3] = x[3];
+    }
+  }
+  const int kv_end = CAUSAL ? min(Nk, qblk * BR + BR) : Nk;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+
+  f32x16_t oacc[DBLK];
+#pragma unroll
+  for (int mb = 0; mb < DBLK; ++mb) oacc[mb] = f32x16_t{};
+  float m2 = -INFINITY, lsum = 0.f;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int tile0 = t * BC;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int ci = tid + 256 * i, r = ci / CH_PER_ROW, c = ci % CH_PER_ROW;
+      const int row = min(tile0 + r, Nk - 1);
+      *(f32x4_t*)&kt[r * RS + 4 * c] = *(const f32x4_t*)(Kh + (int64_t)row * D + 4 * c);
+      *(f32x4_t*)&vt[r * RS + 4 * c] = *(const f32x4_t*)(Vh + (int64_t)row * D + 4 * c);
+    }
+    __syncthreads();
+    if (CAUSAL && tile0 > q_wave0 + 31) continue;
+    f32x16_t s = f32x16_t{};
+    const float* kr = &kt[l32 * RS + hh * HALF];
+#pragma unroll
+    for (int i = 0; i < HALF; i += 4) {
+      const f32x4_t a = *(const f32x4_t*)(kr + i);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], qf[i], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], qf[i + 1], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], qf[i + 2], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], qf[i + 3], s, 0, 0, 0);
+    }
+    const bool need_mask = (tile0 + BC > Nk) || (CAUSAL && tile0 + BC - 1 > q_wave0);
+    if (need_mask) {
+      const int q = q_wave0 + l32;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = tile0 + 8 * (j >> 2) + 4 * hh + (j & 3);
+        if (key >= Nk || (CAUSAL && key > q)) s[j] = -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+    mx = max_across_halves(mx);
+    const float mnew = fmaxf(m2, mx * sl2);
+    const float alpha = fast_exp2(m2 - mnew);
+    m2 = mnew;
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s[j] = fast_exp2(__builtin_fmaf(s[j], sl2, -mnew));
+      rs += s[j];
+    }
+    lsum = alpha * lsum + rs;
+#pragma unroll
+    for (int mb = 0; mb < DBLK; ++mb) {
+      oacc[mb] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int key = 8 * (u >> 2) + 4 * hh + (u & 3);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt[key * RS + 32 * mb + l32], s[u], oacc[mb], 0, 0, 0);
+      }
+    }
+  }
+
+  const float l = sum_across_halves(lsum);
+  const float inv = 1.f / l;
+  const int q = q_wave0 + l32;
+  if (q < Nq) {
+    float* op = O + (int64_t)bh * Nq * D + (int64_t)q * D + 4 * hh;
+#pragma unroll
+    for (int mb = 0; mb < DBLK; ++mb)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        f32x4_t w;
+        w[0] = oacc[mb][4 * jg] * inv; w[1] = oacc[mb][4 * jg + 1] * inv;
+        w[2] = oacc[mb][4 * jg + 2] * inv; w[3] = oacc[mb][4 * jg + 3] * inv;
+        *(f32x4_t*)(op + 32 * mb + 8 * jg) = w;
+      }
+    if (hh == 0) LSE[(int64_t)bh * Nq + q] = (m2 + fast_log2(l)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bf16_impl(const FwdArgs& a, hipStream_t stream) {
+  constexpr int QBLK = 1;
+  using C = Bf16Cfg<D, QBLK>;
+  const int n_qblk = (a.Nq + C::BR - 1) / C::BR;
+  const int64_t nblk = (int64_t)a.B * a.H * n_qblk;
+  const int remap = (nblk % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, QBLK>), dim3((unsigned)nblk), dim3(C::THREADS), 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                     a.Nq, a.Nk, n_qblk, remap, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32_impl(const FwdArgs& a, hipStream_t stream) {
+  const int n_qblk = (a.Nq + 127) / 128;
+  const int64_t nblk = (int64_t)a.B * a.H * n_qblk;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.Nq, a.Nk,
+                     n_qblk, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return a.causal ? launch_bf16_impl<128, true>(a, stream) : launch_bf16_impl<128, false>(a, stream);
+  return a.causal ? launch_bf16_impl<64, true>(a, stream) : launch_bf16_impl<64, false>(a, stream);
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return a.causal ? launch_f32_impl<128, true>(a, stream) : launch_f32_impl<128, false>(a, stream);
+  return a.causal ? launch_f32_impl<64, true>(a, stream) : launch_f32_impl<64, false>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI layer (fa_api.cpp) and the kernel files.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Nq, Nk, d;
+  bool causal;
+  float scale;
+};
+
+struct DecodeSplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o_part;  // [B][H][S][d]
+  float* ml;      // [B][H][S][2]
+  int B, H, Nk, d, num_splits;
+  float scale;
+};
+
+struct DecodeCombineArgs {
+  const float* o_part;
+  const float* ml;
+  void* o;
+  float* lse;
+  int B, H, d, num_splits;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode_split_bf16(const DecodeSplitArgs& a, hipStream_t stream);
+hipError_t launch_decode_split_f32(const DecodeSplitArgs& a, hipStream_t stream);
+hipError_t launch_decode_combine_bf16(const DecodeCombineArgs& a, hipStream_t stream);
+hipError_t launch_decode_combine_f32(const DecodeCombineArgs& a, hipStream_t stream);
+
+}  // namespace fa

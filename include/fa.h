@@ -1,0 +1,100 @@
+/*
+ * fa.h - exact fused attention on AMD MI355X (gfx950): C ABI.
+ *
+ * What is computed.  For every batch b and head h, with Q [Nq, d], K [Nk, d], V [Nk, d]:
+ *     S = scale * Q K^T,  P = softmax(S) row-wise,  O = P V,  LSE_i = ln sum_j exp(S_ij)
+ * This is standard attention as the Day-21 page ("GPU 学习日报 Day 21：FlashAttention：GPU
+ * Memory Hierarchy 下的 IO 优化", §3.1) writes it; the result is exact, only the floating-point
+ * summation order differs from the unfused form (same page, FAQ Q1; M4-047 card
+ * "高效注意力与 FlashAttention", §5).  The GPU never materialises S or P: K/V tiles are staged
+ * through LDS and a running max m, a running sum l and a rescaled accumulator replace them
+ * (Day-21 page §4-§5.3).  LSE is the per-row statistic a backward pass recomputes from
+ * (M4-047 card §3, point (c)).
+ *
+ * Conventions shared by every entry point.
+ *   - Layouts: q, k, v, o are row-major, contiguous [B, H, N, d] (N = Nq for q and o, Nk for
+ *     k and v); lse is [B, H, Nq] float32.  O has the storage type of the inputs.
+ *   - dtype: FA_DTYPE_BF16 (inputs and O bfloat16; fp32 accumulation, P rounded to bf16 with
+ *     round-to-nearest-even before the P V product, O rounded to nearest-even) or FA_DTYPE_F32
+ *     (everything float32, no down-conversion anywhere).
+ *   - scale must be finite and > 0 (1/sqrt(d) in the pages).
+ *   - Every pointer is DEVICE memory owned by the caller.  The library allocates nothing,
+ *     keeps no global mutable state, prints nothing, and is safe to call from several threads.
+ *   - Work is enqueued on `stream` (NULL = the default stream); calls return without
+ *     synchronising.  Inputs must stay valid and unmodified until the work completes.
+ *   - Errors: arguments are validated on the host before any HIP call; on any error nothing is
+ *     launched and a status other than FA_OK is returned.  A failed launch returns FA_ERR_HIP.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_ALIGN = 2,       /* q/k/v/o/workspace not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_SHAPE = 3,       /* a size <= 0, causal with Nq != Nk, or sizes beyond the index limits */
+  FA_ERR_UNSUPPORTED = 4, /* d not in {64, 128}, or unknown dtype */
+  FA_ERR_WORKSPACE = 5,   /* decode workspace smaller than fa_decode_workspace_bytes() */
+  FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  FA_ERR_ARG = 7          /* scale not finite and > 0, or num_splits outside [1, Nk] */
+} fa_status_t;
+
+/*
+ * Fused attention forward (prefill / training forward).
+ *   q [B,H,Nq,d], k and v [B,H,Nk,d]  (in), o [B,H,Nq,d] and lse [B,H,Nq] float32 (out).
+ *   causal != 0 applies the mask "key j is allowed iff j <= i" for query row i; it requires
+ *   Nq == Nk.  Fully masked key tiles are skipped and only tiles on the diagonal are masked
+ *   element by element (Day-21 page §6 table, last row).
+ *   Limits: B*H*ceil(Nq/128) < 2^31 and N*d*sizeof(elt) < 2^31 per head.
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                   int causal, float scale, fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Split-KV decode (one query token per (b, h) against a KV cache): the keys are split into
+ * num_splits contiguous chunks of ceil(Nk / num_splits) keys that are processed in parallel,
+ * then the partial results are merged (Q31 answer, "FlashAttention 为什么快", follow-up 3;
+ * the merge rescales each partial by exp(m_s - max_s m_s), follow-up 2).  A trailing chunk may
+ * be short or empty; the result does not depend on num_splits beyond rounding.
+ *
+ * Workspace (float32, owned by the caller, 16-byte aligned), as written by fa_decode_split
+ * and read by fa_decode_combine:
+ *     float O_part[B][H][num_splits][d];  - sum_j exp(s_j - m_s) v_j over the split (unnormalised)
+ *     float ml[B][H][num_splits][2];      - (m_s, l_s): max score of the split (natural-log units,
+ *                                           -inf for an empty split) and sum_j exp(s_j - m_s)
+ *   ml starts right after O_part.  fa_decode_workspace_bytes returns B*H*num_splits*(d+2)*4.
+ */
+size_t fa_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int num_splits);
+
+/* q [B,H,1,d], k and v [B,H,Nk,d] (in); fills the workspace.  1 <= num_splits <= Nk. */
+fa_status_t fa_decode_split(const void* q, const void* k, const void* v,
+                            void* workspace, size_t workspace_bytes,
+                            int64_t B, int64_t H, int64_t Nk, int64_t d, float scale,
+                            int num_splits, fa_dtype_t dtype, hipStream_t stream);
+
+/* Merges the workspace into o [B,H,1,d] (dtype) and lse [B,H,1] float32. */
+fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t d, int num_splits,
+                              fa_dtype_t dtype, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_string(fa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

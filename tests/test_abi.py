@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports what include/fa.h declares, and rejects bad arguments
+before touching the GPU (CPU only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_126_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# Fake device addresses: validation fails before any of these could be dereferenced.
+P = 0x100000
+P_MIS = 0x100008  # 8-byte aligned only
+BF16, F32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F32
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fa_status_t|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built (python -m exact_attention_126_amd.build)")
+    return fa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared()
+    assert declared == sorted(fa.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(fa_\w+)$", out, re.M))
+    assert set(declared) <= exported
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_single_hip_runtime_mapped(L):
+    maps = open("/proc/self/maps").read()
+    hip = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(hip) == 1, hip
+
+
+def test_status_strings(L):
+    for code in range(8):
+        s = fa.fa_status_string(code)
+        assert s and s != "unknown status"
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=128, Nk=128, d=64, causal=0, scale=0.125, dtype=BF16):
+    vp = ctypes.c_void_p
+    return L.fa_fwd(vp(q) if q else None, vp(k) if k else None, vp(v) if v else None, vp(o) if o else None,
+                    vp(lse) if lse else None, B, H, Nq, Nk, d, causal, scale, dtype, None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, q=0) == 1 and fwd(L, lse=0) == 1
+    assert fwd(L, d=96) == 4 and fwd(L, d=256) == 4 and fwd(L, dtype=7) == 4
+    assert fwd(L, k=P_MIS) == 2 and fwd(L, o=P + 4) == 2 and fwd(L, lse=P + 2) == 2
+    assert fwd(L, lse=P + 4, scale=0.0) == 7  # a 4-byte aligned lse passes the alignment check
+    assert fwd(L, B=0) == 3 and fwd(L, H=-1) == 3 and fwd(L, Nq=0) == 3 and fwd(L, Nk=0) == 3
+    assert fwd(L, causal=1, Nq=128, Nk=256) == 3
+    assert fwd(L, Nq=2**31 // 128, d=128) == 3  # one head beyond 2^31 bytes
+    assert fwd(L, B=2**20, H=2**20) == 3
+    assert fwd(L, scale=0.0) == 7 and fwd(L, scale=-1.0) == 7 and fwd(L, scale=float("inf")) == 7
+    assert fwd(L, scale=float("nan")) == 7
+
+
+def test_decode_workspace_bytes(L):
+    assert fa.fa_decode_workspace_bytes(16, 32, 128, 64) == 16 * 32 * 64 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(0, 32, 128, 64) == 0
+    assert fa.fa_decode_workspace_bytes(1, 1, 64, 0) == 0
+
+
+def split(L, q=P, k=P, v=P, ws=P, wsb=None, B=2, H=3, Nk=100, d=128, scale=0.1, S=4, dtype=BF16):
+    vp = ctypes.c_void_p
+    if wsb is None:
+        wsb = fa.fa_decode_workspace_bytes(B, H, d, S) if S > 0 else 0
+    return L.fa_decode_split(vp(q) if q else None, vp(k) if k else None, vp(v) if v else None,
+                             vp(ws) if ws else None, wsb, B, H, Nk, d, scale, S, dtype, None)
+
+
+def test_decode_split_validation(L):
+    assert split(L, ws=0) == 1 and split(L, q=0) == 1
+    assert split(L, d=32) == 4 and split(L, dtype=3) == 4
+    assert split(L, ws=P + 8) == 2 and split(L, v=P_MIS) == 2
+    assert split(L, Nk=0) == 3 and split(L, B=0) == 3
+    assert split(L, S=0, wsb=1 << 20) == 7 and split(L, S=101) == 7 and split(L, scale=0.0) == 7
+    need = fa.fa_decode_workspace_bytes(2, 3, 128, 4)
+    assert split(L, wsb=need - 1) == 5
+
+
+def combine(L, ws=P, wsb=None, o=P, lse=P, B=2, H=3, d=64, S=4, dtype=F32):
+    vp = ctypes.c_void_p
+    if wsb is None:
+        wsb = fa.fa_decode_workspace_bytes(B, H, d, S) if S > 0 else 0
+    return L.fa_decode_combine(vp(ws) if ws else None, wsb, vp(o) if o else None, vp(lse) if lse else None,
+                               B, H, d, S, dtype, None)
+
+
+def test_decode_combine_validation(L):
+    assert combine(L, o=0) == 1 and combine(L, lse=0) == 1
+    assert combine(L, d=100) == 4
+    assert combine(L, o=P + 8) == 2
+    assert combine(L, H=0) == 3
+    assert combine(L, S=0, wsb=1 << 20) == 7
+    assert combine(L, wsb=fa.fa_decode_workspace_bytes(2, 3, 64, 4) - 4) == 5
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q)
