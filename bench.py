@@ -1,0 +1,261 @@
+"""Benchmark of the exact fused attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-baseline on|off] [--copy-calibration]
+
+One step is one pass of the whole path over one batch of synthetic input:
+  * the fused causal forward (fa_fwd) on B=8, H=16, Nq=Nk=8192, d=128, bf16, K scaled x2;
+  * one-token split-KV decode (fa_decode_split + fa_decode_combine) on B=16, H=32,
+    Nk=32768, d=128, bf16, 64 splits.
+Inputs are generated on the host from the seeded recipe, copied to HBM once, and stay
+resident; the timed region holds only kernel launches.  Every launch is bracketed by HIP
+events on the stream it runs on, so per-kernel average durations come from the GPU clock.
+
+The printed JSON line carries:
+  value        forward TFLOP/s = 4*B*H*Nq*Nk*d / 2 (causal) / mean fa_fwd duration
+  roofline     the forward kernel against the dense bf16 MFMA peak (2516.6 TFLOP/s)
+  decode       decode KV-read GB/s (K and V read once) with its own HBM roofline
+  cpu_baseline the float64 reference implementation timed on the host cores on a sample
+               of the same workload (a reported baseline only)
+HBM traffic measured with rocprofv3 counters is read from profiles/ when the summary there
+was taken on the current kernel sources, else reported as null.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PREFILL = "prefill_b8h16_n8192_d128_causal"
+DECODE = "decode_b16h32_nk32768_d128"
+FWD_SOURCES = ["exact_attention_126_amd/csrc/fa_fwd.hip", "exact_attention_126_amd/csrc/fa_device.h"]
+DEC_SOURCES = ["exact_attention_126_amd/csrc/fa_decode.hip", "exact_attention_126_amd/csrc/fa_device.h"]
+
+
+def sources_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str, paths) -> dict | None:
+    """Counter-derived HBM bytes per launch from profiles/<name>, if it matches the sources."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith((" ", "#", "|", "`")):
+                k, v = ln.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256_16") != sources_sha(paths):
+        return None
+    try:
+        return {"bytes": float(kv["traffic_bytes_per_launch"]), "read": float(kv["read_bytes_per_launch"]),
+                "write": float(kv["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------- CPU baseline (oracle)
+def _oracle_prefill_head(args):
+    import threadpoolctl
+    import oracle
+    from synth import inputs as si
+    from synth.workloads import get
+    w = get(PREFILL)
+    b, h = args
+    with threadpoolctl.threadpool_limits(1):
+        q, k, v = (si.head_block_f32(w, x, b, h) for x in "qkv")
+        t0 = time.perf_counter()
+        oracle.attention_head(q, k, v, w.scale, w.causal)
+        return time.perf_counter() - t0
+
+
+def _oracle_decode_head(args):
+    import threadpoolctl
+    import oracle
+    from synth import inputs as si
+    from synth.workloads import get
+    w = get(DECODE)
+    b, h = args
+    with threadpoolctl.threadpool_limits(1):
+        q, k, v = (si.head_block_f32(w, x, b, h) for x in "qkv")
+        t0 = time.perf_counter()
+        oracle.attention_head(q, k, v, w.scale, False)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline():
+    """Time the float64 reference on the host cores, on whole heads of the two workloads.
+
+    Runs before anything touches the GPU: the worker processes are forked from a process
+    that has not initialised the HIP runtime.  Each worker uses one BLAS thread."""
+    import multiprocessing as mp
+    from synth.workloads import get
+    cores = min(16, len(os.sched_getaffinity(0)))
+    wp, wd = get(PREFILL), get(DECODE)
+    n_pre = 2 * cores  # whole heads of batch 0 (and 1 on a wide host)
+    pre_heads = [(i // wp.H, i % wp.H) for i in range(n_pre)]
+    dec_heads = [(i // wd.H, i % wd.H) for i in range(4 * cores)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        t0 = time.perf_counter()
+        pool.map(_oracle_prefill_head, pre_heads, chunksize=1)
+        t_pre = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        pool.map(_oracle_decode_head, dec_heads, chunksize=1)
+        t_dec = time.perf_counter() - t0
+    flops = 4.0 * len(pre_heads) * wp.Nq * wp.Nk * wp.d / 2
+    kv_bytes = 2 * len(dec_heads) * wd.Nk * wd.d * wd.elt_bytes
+    prefill = {"value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": f"{len(pre_heads)} of {wp.B * wp.H} heads of {PREFILL} (whole heads; float64; the "
+                         f"reference builds the full masked score matrix, counted at the causal FLOP formula), "
+                         f"{t_pre:.2f} s wall"}
+    decode = {"value": kv_bytes / t_dec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+              "sample": f"{len(dec_heads)} of {wd.B * wd.H} heads of {DECODE} (float64), {t_dec:.2f} s wall"}
+    return prefill, decode
+
+
+# ----------------------------------------------------------------- GPU part
+def to_device(w, x):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (reference point for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards over "
+              f"(batch, head) with no communication, so N GPUs run N independent copies of this step).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from synth import inputs as si
+    from synth.workloads import get
+
+    cpu_pre = cpu_dec = None
+    if args.cpu_baseline == "on":
+        print("[bench] timing the float64 reference on host cores ...", file=sys.stderr, flush=True)
+        cpu_pre, cpu_dec = cpu_baseline()
+        print(f"[bench] cpu baseline: {cpu_pre['value']:.4f} TFLOP/s, {cpu_dec['value']:.2f} GB/s "
+              f"on {cpu_pre['cores']} cores", file=sys.stderr, flush=True)
+
+    import torch
+    import exact_attention_126_amd as fa
+
+    wp, wd = get(PREFILL), get(DECODE)
+    t0 = time.perf_counter()
+    dp = {x: to_device(wp, si.make_tensor(wp, x)) for x in "qkv"}
+    dd = {}
+    for x in "qkv":
+        dd[x] = to_device(wd, si.make_tensor(wd, x))
+    print(f"[bench] inputs generated and resident in HBM in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+
+    o = torch.empty_like(dp["q"])
+    lse = torch.empty((wp.B, wp.H, wp.Nq), dtype=torch.float32, device="cuda")
+    od = torch.empty_like(dd["q"])
+    lsed = torch.empty((wd.B, wd.H, 1), dtype=torch.float32, device="cuda")
+    ws = fa.decode_workspace(dd["q"], wd.num_splits)
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(rec=None):
+        e = [ev() for _ in range(4)] if rec is not None else None
+        if e: e[0].record(stream)
+        fa.fa_fwd(dp["q"], dp["k"], dp["v"], o, lse, causal=True, scale=wp.scale, stream=stream)
+        if e: e[1].record(stream)
+        fa.fa_decode_split(dd["q"], dd["k"], dd["v"], ws, wd.num_splits, wd.scale, stream=stream)
+        if e: e[2].record(stream)
+        fa.fa_decode_combine(ws, od, lsed, wd.num_splits, stream=stream)
+        if e: e[3].record(stream)
+        if rec is not None:
+            rec.append(e)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 1 GiB read + 1 GiB written by one device copy", file=sys.stderr, flush=True)
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rec = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_fwd = [a.elapsed_time(b) for a, b, _, _ in rec]
+    t_split = [b.elapsed_time(c) for _, b, c, _ in rec]
+    t_comb = [c.elapsed_time(d) for _, _, c, d in rec]
+    ms_fwd = sum(t_fwd) / len(t_fwd)
+    ms_split = sum(t_split) / len(t_split)
+    ms_comb = sum(t_comb) / len(t_comb)
+    flops = 4.0 * wp.B * wp.H * wp.Nq * wp.Nk * wp.d / 2
+    tflops = flops / (ms_fwd * 1e-3) / 1e12
+    kv_bytes = 2.0 * wd.B * wd.H * wd.Nk * wd.d * wd.elt_bytes
+    dec_gbs = kv_bytes / ((ms_split + ms_comb) * 1e-3) / 1e9
+    split_gbs = kv_bytes / (ms_split * 1e-3) / 1e9
+
+    tr_f = read_traffic("fwd_bf16_prefill_b8h16_n8192_d128_causal_hbm_traffic.txt", FWD_SOURCES)
+    tr_d = read_traffic("decode_split_b16h32_nk32768_d128_hbm_traffic.txt", DEC_SOURCES)
+    line = {
+        "metric": "fwd attention TFLOP/s & % bf16 MFMA peak at N=8K d=128; decode KV GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded PCG64 N(0,1), rounded to bf16)",
+        "config": {"workload": f"{PREFILL} + {DECODE}", "prefill": "B=8 H=16 Nq=Nk=8192 d=128 causal, K x2",
+                   "decode": "B=16 H=32 Nq=1 Nk=32768 d=128, 64 splits", "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(ms_fwd, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "kernel": "fwd_bf16_kernel<128, causal>",
+                     "traffic": None if tr_f is None else tr_f["bytes"]},
+        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "pct_of_hbm_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
+                   "split_ms": round(ms_split, 4), "combine_ms": round(ms_comb, 4),
+                   "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(split_gbs / PEAK_HBM_GBS, 4), "kernel": "decode_split_kernel<bf16, 128>",
+                                "traffic": None if tr_d is None else tr_d["bytes"]},
+                   "cpu_baseline": cpu_dec},
+        "cpu_baseline": cpu_pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,8 +22,14 @@
 //  * LDS rows are XOR-swizzled in 16-byte chunks by the row's low four bits, chosen so that
 //    the tile stores, the K operand reads and the transposing V reads are all free of bank
 //    conflicts.
-//  * K/V tiles are double-buffered: tile t+1 is fetched into registers while tile t is
-//    consumed, and stored to the other LDS stage afterwards; one barrier per tile.
+//  * K/V tiles are double-buffered in LDS and fetched with global_load_lds_dwordx4, which
+//    writes HBM/L2 data straight into LDS without passing through VGPRs: tile t+1 streams in
+//    while tile t is consumed; one barrier per tile.  Every workgroup needs 64 KiB (d=128) of
+//    LDS and at most 256 VGPRs per lane, so two workgroups (two waves per SIMD) share a CU and
+//    one wave's MFMA work overlaps the other's softmax.
+//  * The running max is raised lazily: the O_acc rescale is skipped unless some row's max grew
+//    by more than 2^8 (the exponentials stay below 256; the result does not depend on the
+//    subtracted value).
 //  * Causal: tiles wholly after a wave's last query are skipped, tiles crossing the diagonal
 //    are masked element by element (Day-21 page §6 table), and the query blocks with the
 //    most tiles are dispatched first.  Workgroups are remapped so that the ones an XCD runs
@@ -55,34 +61,43 @@ __device__ __forceinline__ int key_of_row(int r) {
   return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
-template <int D, int QBLK>
+template <int D>
 struct Bf16Cfg {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int BR = WAVES * 32 * QBLK;  // query rows per workgroup
-  static constexpr int BC = 64;                 // keys per tile
-  static constexpr int RB = D * 2;              // bytes per LDS row
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int BR = WAVES * 32;  // query rows per workgroup, 32 per wave
+  static constexpr int BC = 64;          // keys per tile
+  static constexpr int RB = D * 2;       // bytes per LDS row
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int TILE_BYTES = BC * RB;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile then V tile
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static constexpr int KSTEPS = D / 16;                     // MFMA k-steps of S^T = K Q^T
-  static constexpr int DBLK = D / 32;                       // 32-dim blocks of O^T
-  static constexpr int CHUNKS = TILE_BYTES / 16 / THREADS;  // 16-byte chunks per thread per tensor
-  static constexpr int ROWS_PER_PASS = THREADS / CPR;
-  static_assert(ROWS_PER_PASS % 16 == 0, "swizzle must be invariant across a thread's rows");
+  static constexpr int ROWS_PER_DMA = 64 / CPR;                     // rows one wave-wide 1 KiB LDS load fills
+  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / WAVES;    // per tensor and tile
+  static constexpr int KSTEPS = D / 16;                             // MFMA k-steps of S^T = K Q^T
+  static constexpr int DBLK = D / 32;                               // 32-dim blocks of O^T
+  static_assert(TILE_BYTES % (1024 * WAVES) == 0, "tile must split evenly into wave loads");
 };
+
+// Lazy rescaling threshold, log2 units: the running max used for the exponentials is only
+// raised when a tile's row max exceeds it by more than this, so most tiles skip the
+// O_acc rescale.  Exponentials are then bounded by 2^kLazyRescale (exact: softmax does not
+// depend on the value subtracted, Day-21 page §5.2).
+constexpr float kLazyRescale = 8.f;
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-template <int D, bool CAUSAL, int QBLK>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int xcd_remap,
     float sl2) {
-  using C = Bf16Cfg<D, QBLK>;
-  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
-  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  using C = Bf16Cfg<D>;
+  // Two LDS stages, each a K tile followed by a V tile.  Separate arrays let the compiler see
+  // that reads of one stage never alias the asynchronous loads into the other.
+  __shared__ __attribute__((aligned(1024))) char stage0[2 * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stage1[2 * C::TILE_BYTES];
 
   // ---- workgroup -> (batch*head, query block)
   int bid = blockIdx.x;
@@ -96,41 +111,41 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   const uint16_t* Vh = V + (int64_t)bh * Nk * D;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-  const int q_wave0 = qblk * C::BR + wave * 32 * QBLK;
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q_wave0 = qblk * C::BR + wave * 32;  // first query of this wave (wave-uniform)
 
   // ---- Q^T fragments (B operand), resident for the whole kernel
-  bf16x8_t qf[QBLK][C::KSTEPS];
-#pragma unroll
-  for (int qb = 0; qb < QBLK; ++qb) {
-    const int qrow = min(q_wave0 + 32 * qb + l32, Nq - 1);
+  bf16x8_t qf[C::KSTEPS];
+  {
+    const int qrow = min(q_wave0 + l32, Nq - 1);
     const uint16_t* qp = Qh + (int64_t)qrow * D + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[qb][ks] = as_bf16x8(gload16(qp + 16 * ks));
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = as_bf16x8(gload16(qp + 16 * ks));
   }
 
-  // ---- tile range
+  // ---- tile range of the workgroup
   const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR) : Nk;
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
 
-  // ---- staging: thread tid moves chunks tid + THREADS*i of each tile
-  const int st_row0 = tid / C::CPR, st_c = tid % C::CPR;
-  const int st_lds = st_row0 * C::RB + ((st_c ^ swz<D>(st_row0)) << 4);
-  u32x4_t kreg[C::CHUNKS], vreg[C::CHUNKS];
-  auto load_tile = [&](int t) {
+  // ---- asynchronous global -> LDS tile loads.  One instruction moves 16 bytes per lane into
+  // 1 KiB of consecutive LDS; lane L lands in row L / CPR, slot L % CPR of its rows, so it
+  // fetches the global chunk that the row's swizzle puts in that slot.
+  int dma_row[C::DMA_PER_WAVE], dma_col[C::DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < C::CHUNKS; ++i) {
-      const int row = min(t * C::BC + st_row0 + i * C::ROWS_PER_PASS, Nk - 1);
-      kreg[i] = gload16(Kh + (int64_t)row * D + st_c * 8);
-      vreg[i] = gload16(Vh + (int64_t)row * D + st_c * 8);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    FA_LDS char* base = smem + stage * C::STAGE_BYTES + st_lds;
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int row = (wave * C::DMA_PER_WAVE + i) * C::ROWS_PER_DMA + lane / C::CPR;
+    dma_row[i] = row;
+    dma_col[i] = ((lane % C::CPR) ^ swz<D>(row)) * 8;
+  }
+  auto issue_tile = [&](int t, char* stage) {
+    const int tile0 = t * C::BC;
 #pragma unroll
-    for (int i = 0; i < C::CHUNKS; ++i) {
-      lds_store16(base + i * C::ROWS_PER_PASS * C::RB, kreg[i]);
-      lds_store16(base + C::TILE_BYTES + i * C::ROWS_PER_PASS * C::RB, vreg[i]);
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const int64_t off = (int64_t)min(tile0 + dma_row[i], Nk - 1) * D + dma_col[i];
+      char* dst = stage + (wave * C::DMA_PER_WAVE + i) * 1024;
+      __builtin_amdgcn_global_load_lds((gptr_t)(Kh + off), (lptr_t)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)(Vh + off), (lptr_t)(dst + C::TILE_BYTES), 16, 0, 0);
     }
   };
 
@@ -152,128 +167,110 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       for (int I = 0; I < 2; ++I) {
         const int key = 8 * vh + 4 * I + ve;
         const int dim = 32 * mb + 16 * (g & 1) + 4 * vq;
-        voff[mb][I] = key * C::RB + (((dim >> 3) ^ swz<D>(key)) << 4) + ((dim >> 2) & 1) * 8;
+        voff[mb][I] = C::TILE_BYTES + key * C::RB + (((dim >> 3) ^ swz<D>(key)) << 4) + ((dim >> 2) & 1) * 8;
       }
   }
 
-  f32x16_t oacc[QBLK][C::DBLK];
-  float m2[QBLK], lsum[QBLK];
+  f32x16_t oacc[C::DBLK];
 #pragma unroll
-  for (int qb = 0; qb < QBLK; ++qb) {
-    m2[qb] = -INFINITY;
-    lsum[qb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < C::DBLK; ++mb) oacc[qb][mb] = f32x16_t{};
-  }
+  for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] = f32x16_t{};
+  float m2 = -INFINITY, lsum = 0.f;
 
-  auto tile_compute = [&](auto mask_tag, const FA_LDS char* kt, const FA_LDS char* vt, int tile0) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    // S^T = K Q^T for the two 32-key blocks of the tile
-    f32x16_t sacc[QBLK][2];
-#pragma unroll
-    for (int qb = 0; qb < QBLK; ++qb) sacc[qb][0] = sacc[qb][1] = f32x16_t{};
+  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile_compute = [&](const char* st, int tile0, bool need_mask) {
+    const FA_LDS char* kt = (const FA_LDS char*)st;
+    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       const bf16x8_t a0 = as_bf16x8(lds_load16(kt + koff[ks]));
       const bf16x8_t a1 = as_bf16x8(lds_load16(kt + 32 * C::RB + koff[ks]));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+    }
+    if (need_mask) {  // wave-uniform: the tile crosses the diagonal or the end of the keys
+      const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32) : Nk - 1;  // last allowed key of this lane's query
 #pragma unroll
-      for (int qb = 0; qb < QBLK; ++qb) {
-        sacc[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[qb][ks], sacc[qb][0], 0, 0, 0);
-        sacc[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[qb][ks], sacc[qb][1], 0, 0, 0);
+      for (int j = 0; j < 16; ++j) {
+        const int key = tile0 + 16 * (j >> 3) + 8 * hh + (j & 7);
+        if (key > lim) s0[j] = -INFINITY;
+        if (key + 32 > lim) s1[j] = -INFINITY;
       }
     }
-    // online softmax (log2 domain) and P^T packing
-    u32x4_t pb[QBLK][4];
+    // running max (log2 units), raised lazily
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int qb = 0; qb < QBLK; ++qb) {
-      if (MASK) {
-        const int q = q_wave0 + 32 * qb + l32;
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
+    mx = max_across_halves(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
+      const float mnew = fmaxf(m2, mx);
+      const float alpha = fast_exp2(m2 - mnew);
+      m2 = mnew;
+      lsum *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] *= alpha;
+    }
+    // P^T = exp2(S^T * scale * log2 e - m) in groups of 16 keys; each group, packed to bf16,
+    // is the B operand of one k-step of O^T += V^T P^T.
+    const float nm = -m2;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = tile0 + 32 * kb + 16 * (j >> 3) + 8 * hh + (j & 7);
-            if (key >= Nk || (CAUSAL && key > q)) sacc[qb][kb][j] = -INFINITY;
-          }
-      }
-      float mx = sacc[qb][0][0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[qb][0][j]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[qb][1][j]);
-      mx = max_across_halves(mx);
-      const float mnew = fmaxf(m2[qb], mx * sl2);
-      const float alpha = fast_exp2(m2[qb] - mnew);
-      m2[qb] = mnew;
+    for (int t = 0; t < 4; ++t) {
+      const f32x16_t& s = (t < 2) ? s0 : s1;
+      const int j0 = 8 * (t & 1);
+      u32x4_t pb;
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[qb][kb][2 * jj], sl2, -mnew));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[qb][kb][2 * jj + 1], sl2, -mnew));
-          rs += p0 + p1;
-          pb[qb][2 * kb + (jj >> 2)][jj & 3] = pack_bf16x2(p0, p1);
-        }
-      lsum[qb] = alpha * lsum[qb] + rs;
-#pragma unroll
-      for (int mb = 0; mb < C::DBLK; ++mb) oacc[qb][mb] *= alpha;
-    }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int mb = 0; mb < C::DBLK; ++mb)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const i16x4_t lo = lds_load8_tr16(vt + voff[mb][0] + t * 16 * C::RB);
-        const i16x4_t hi = lds_load8_tr16(vt + voff[mb][1] + t * 16 * C::RB);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < QBLK; ++qb)
-          oacc[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[qb][t]), oacc[qb][mb], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) {
+        const float pa = fast_exp2(__builtin_fmaf(s[j0 + 2 * u], sl2, nm));
+        const float pc = fast_exp2(__builtin_fmaf(s[j0 + 2 * u + 1], sl2, nm));
+        rs += pa + pc;
+        pb[u] = pack_bf16x2(pa, pc);
       }
+      lsum += rs;
+#pragma unroll
+      for (int mb = 0; mb < C::DBLK; ++mb) {
+        const i16x4_t lo = lds_load8_tr16(kt + voff[mb][0] + t * 16 * C::RB);
+        const i16x4_t hi = lds_load8_tr16(kt + voff[mb][1] + t * 16 * C::RB);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb), oacc[mb], 0, 0, 0);
+      }
+    }
   };
 
-  // ---- main loop over K/V tiles
-  load_tile(0);
-  store_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();  // stage t&1 is complete; stage (t+1)&1 is no longer read
-    if (t + 1 < n_tiles) load_tile(t + 1);
+  // One step of the tile loop: wait until tile t is in `cur`, start loading tile t + 1 into
+  // `nxt` (everyone has finished reading it: it held tile t - 1), then compute tile t.
+  auto step = [&](int t, const char* cur, char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t have landed
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(t + 1, nxt);
     const int tile0 = t * C::BC;
-    const FA_LDS char* kt = smem + (t & 1) * C::STAGE_BYTES;
-    const FA_LDS char* vt = kt + C::TILE_BYTES;
-    const bool active = !CAUSAL || tile0 <= q_wave0 + 32 * QBLK - 1;
-    if (active) {
-      const bool need_mask = (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0);
-      if (need_mask)
-        tile_compute(std::integral_constant<bool, true>{}, kt, vt, tile0);
-      else
-        tile_compute(std::integral_constant<bool, false>{}, kt, vt, tile0);
-    }
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+    if (!CAUSAL || tile0 <= q_wave0 + 31)
+      tile_compute(cur, tile0, (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0));
+  };
+
+  issue_tile(0, stage0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, stage0, stage1);
+    if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
   }
 
   // ---- epilogue: O = O_acc / l (RNE to bf16), LSE = (m + log2 l) * ln 2
   uint16_t* Oh = O + (int64_t)bh * Nq * D;
   float* Lh = LSE + (int64_t)bh * Nq;
+  const float l = sum_across_halves(lsum);
+  const float inv = 1.f / l;
+  const int q = q_wave0 + l32;
+  if (q < Nq) {
+    uint16_t* op = Oh + (int64_t)q * D + 4 * hh;
 #pragma unroll
-  for (int qb = 0; qb < QBLK; ++qb) {
-    const float l = sum_across_halves(lsum[qb]);
-    const float inv = 1.f / l;
-    const int q = q_wave0 + 32 * qb + l32;
-    if (q < Nq) {
-      uint16_t* op = Oh + (int64_t)q * D + 4 * hh;
+    for (int mb = 0; mb < C::DBLK; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < C::DBLK; ++mb)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          u32x2_t w;
-          w[0] = pack_bf16x2(oacc[qb][mb][4 * jg + 0] * inv, oacc[qb][mb][4 * jg + 1] * inv);
-          w[1] = pack_bf16x2(oacc[qb][mb][4 * jg + 2] * inv, oacc[qb][mb][4 * jg + 3] * inv);
-          *(u32x2_t*)(op + 32 * mb + 8 * jg) = w;
-        }
-      if (hh == 0) Lh[q] = (m2[qb] + fast_log2(l)) * kLn2;
-    }
+      for (int jg = 0; jg < 4; ++jg) {
+        u32x2_t w;
+        w[0] = pack_bf16x2(oacc[mb][4 * jg + 0] * inv, oacc[mb][4 * jg + 1] * inv);
+        w[1] = pack_bf16x2(oacc[mb][4 * jg + 2] * inv, oacc[mb][4 * jg + 3] * inv);
+        *(u32x2_t*)(op + 32 * mb + 8 * jg) = w;
+      }
+    if (hh == 0) Lh[q] = (m2 + fast_log2(l)) * kLn2;
   }
 }
 
@@ -396,12 +393,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_impl(const FwdArgs& a, hipStream_t stream) {
-  constexpr int QBLK = 1;
-  using C = Bf16Cfg<D, QBLK>;
+  using C = Bf16Cfg<D>;
   const int n_qblk = (a.Nq + C::BR - 1) / C::BR;
   const int64_t nblk = (int64_t)a.B * a.H * n_qblk;
   const int remap = (nblk % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, QBLK>), dim3((unsigned)nblk), dim3(C::THREADS), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(C::THREADS), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.Nq, a.Nk, n_qblk, remap, a.scale * kLog2e);
   return hipGetLastError();
