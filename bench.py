@@ -40,10 +40,15 @@ DEC_SOURCES = ["exact_attention_126_amd/csrc/fa_decode.hip", "exact_attention_12
 
 
 def sources_sha(paths) -> str:
+    """Hash of the kernel sources with // comments and whitespace removed, so that editing a
+    comment does not invalidate counter figures taken on the same code."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            for ln in f:
+                code = ln.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode())
     return h.hexdigest()[:16]
 
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace fa {
 
@@ -39,6 +40,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2_t v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// max(a, b, c) in one v_max3_f32.  fmaxf on values the compiler cannot prove canonical (MFMA
+// results) first quiets each input with an extra v_max_f32; scores are never NaN here.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // Max of a value across the two 32-lane halves of a wave (lane l and lane l ^ 32).

@@ -22,17 +22,22 @@
 //  * LDS rows are XOR-swizzled in 16-byte chunks by the row's low four bits, chosen so that
 //    the tile stores, the K operand reads and the transposing V reads are all free of bank
 //    conflicts.
-//  * K/V tiles are double-buffered in LDS and fetched with global_load_lds_dwordx4, which
-//    writes HBM/L2 data straight into LDS without passing through VGPRs: tile t+1 streams in
-//    while tile t is consumed; one barrier per tile.  Every workgroup needs 64 KiB (d=128) of
-//    LDS and at most 256 VGPRs per lane, so two workgroups (two waves per SIMD) share a CU and
-//    one wave's MFMA work overlaps the other's softmax.
+//  * Ping-pong.  A workgroup is eight waves in two groups of four; each SIMD runs one wave of
+//    each group (at most 256 VGPRs per lane, one workgroup per CU).  Workgroup barriers cut
+//    time into half-periods; in each, one group issues the MFMAs of S_j and of O += P_{j-1}
+//    V_{j-1} while the other runs the softmax of its tile on the VALU, and the groups swap.
+//    Empty asm statements that take the phase's results as operands keep the compiler from
+//    moving one phase's arithmetic into the next.
+//  * K/V tiles live in two-slot LDS rings and are fetched with global_load_lds_dwordx4, which
+//    writes HBM/L2 data straight into LDS without passing through VGPRs; the loads are issued
+//    by group 0 inside its MFMA phases and have two half-periods to land.
 //  * The running max is raised lazily: the O_acc rescale is skipped unless some row's max grew
 //    by more than 2^8 (the exponentials stay below 256; the result does not depend on the
 //    subtracted value).
-//  * Causal: tiles wholly after a wave's last query are skipped, tiles crossing the diagonal
-//    are masked element by element (Day-21 page §6 table), and the query blocks with the
-//    most tiles are dispatched first.  Workgroups are remapped so that the ones an XCD runs
+//  * Causal: every wave processes all the tiles its workgroup needs and masks, element by
+//    element, the tiles that reach past its own diagonal (a tile wholly past it contributes
+//    nothing); uniform work keeps the two groups in lockstep.  Query blocks with the most
+//    tiles are dispatched first, and workgroups are remapped so that the ones an XCD runs
 //    together share a head's K/V in that XCD's L2.
 //  * exp is the hardware exp2 with scale * log2(e) folded into one FMA; LSE is emitted in
 //    natural-log units.
@@ -63,7 +68,7 @@ __device__ __forceinline__ int key_of_row(int r) {
 
 template <int D>
 struct Bf16Cfg {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = 8;        // two groups of four, one wave of each per SIMD
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BR = WAVES * 32;  // query rows per workgroup, 32 per wave
   static constexpr int BC = 64;          // keys per tile
@@ -71,10 +76,11 @@ struct Bf16Cfg {
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int TILE_BYTES = BC * RB;
   static constexpr int ROWS_PER_DMA = 64 / CPR;                     // rows one wave-wide 1 KiB LDS load fills
-  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / WAVES;    // per tensor and tile
+  static constexpr int LOADERS = 4;                                 // waves of group 0 move the tiles
+  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / LOADERS;  // per tensor and tile
   static constexpr int KSTEPS = D / 16;                             // MFMA k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 32;                               // 32-dim blocks of O^T
-  static_assert(TILE_BYTES % (1024 * WAVES) == 0, "tile must split evenly into wave loads");
+  static_assert(TILE_BYTES % (1024 * LOADERS) == 0, "tile must split evenly into wave loads");
 };
 
 // Lazy rescaling threshold, log2 units: the running max used for the exponentials is only
@@ -83,21 +89,47 @@ struct Bf16Cfg {
 // depend on the value subtracted, Day-21 page §5.2).
 constexpr float kLazyRescale = 8.f;
 
+#ifndef FA_KA
+#define FA_KA 8
+#endif
+#ifndef FA_VA
+#define FA_VA 4
+#endif
+
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time loop).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Eight waves: group 0 (waves 0-3) and group 1 (waves 4-7) each cover the four SIMDs, so every
+// SIMD runs one wave of each group.  Time is cut into half-periods separated by workgroup
+// barriers.  In half-period h a wave of group g works on phase p = h - g:
+//   p = 2j     MFMA phase j:    S_j = K_j Q^T, then O += P_{j-1} V_{j-1}
+//   p = 2j + 1 softmax phase j: max, lazy rescale, P_j = exp2(S_j - m) (VALU)
+// so on every SIMD one wave feeds the matrix core while the other runs its softmax.  Loads of
+// K_{j+1} and V_j start at half-period 2j and are complete two half-periods later.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int xcd_remap,
     float sl2) {
   using C = Bf16Cfg<D>;
-  // Two LDS stages, each a K tile followed by a V tile.  Separate arrays let the compiler see
-  // that reads of one stage never alias the asynchronous loads into the other.
-  __shared__ __attribute__((aligned(1024))) char stage0[2 * C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char stage1[2 * C::TILE_BYTES];
+  // Two-slot rings for K and V tiles.  Separate arrays let the compiler see that reads of one
+  // slot never alias the asynchronous loads into another.
+  __shared__ __attribute__((aligned(1024))) char kb0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[C::TILE_BYTES];
 
   // ---- workgroup -> (batch*head, query block)
   int bid = blockIdx.x;
@@ -113,6 +145,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
   const int q_wave0 = qblk * C::BR + wave * 32;  // first query of this wave (wave-uniform)
 
   // ---- Q^T fragments (B operand), resident for the whole kernel
@@ -124,28 +157,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = as_bf16x8(gload16(qp + 16 * ks));
   }
 
-  // ---- tile range of the workgroup
+  // ---- the workgroup streams n tiles and every wave processes all of them
   const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR) : Nk;
-  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  const int n = (kv_end + C::BC - 1) / C::BC;
 
-  // ---- asynchronous global -> LDS tile loads.  One instruction moves 16 bytes per lane into
-  // 1 KiB of consecutive LDS; lane L lands in row L / CPR, slot L % CPR of its rows, so it
-  // fetches the global chunk that the row's swizzle puts in that slot.
-  int dma_row[C::DMA_PER_WAVE], dma_col[C::DMA_PER_WAVE];
+  // ---- asynchronous global -> LDS tile loads, issued by the four waves of group 0 inside their
+  // MFMA phases (their vector units are idle there).  One instruction moves 16 bytes per lane
+  // into 1 KiB of consecutive LDS; lane L lands in row L / CPR, slot L % CPR of its rows, so it
+  // fetches the global chunk that the row's swizzle puts in that slot.  Addresses are the head's
+  // base (scalar) plus a 32-bit per-lane byte offset; rows past the end of the keys are clamped
+  // to the last key (their scores are masked).
+  const int lw = wave & 3;
+  int dma_row[C::DMA_PER_WAVE], dma_cb[C::DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-    const int row = (wave * C::DMA_PER_WAVE + i) * C::ROWS_PER_DMA + lane / C::CPR;
+    const int row = (lw * C::DMA_PER_WAVE + i) * C::ROWS_PER_DMA + lane / C::CPR;
     dma_row[i] = row;
-    dma_col[i] = ((lane % C::CPR) ^ swz<D>(row)) * 8;
+    dma_cb[i] = ((lane % C::CPR) ^ swz<D>(row)) * 16;
   }
-  auto issue_tile = [&](int t, char* stage) {
+  auto issue = [&](const uint16_t* src, int t, char* buf) {
     const int tile0 = t * C::BC;
+    const char* sb = (const char*)src;
 #pragma unroll
     for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      const int64_t off = (int64_t)min(tile0 + dma_row[i], Nk - 1) * D + dma_col[i];
-      char* dst = stage + (wave * C::DMA_PER_WAVE + i) * 1024;
-      __builtin_amdgcn_global_load_lds((gptr_t)(Kh + off), (lptr_t)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gptr_t)(Vh + off), (lptr_t)(dst + C::TILE_BYTES), 16, 0, 0);
+      const uint32_t off = (uint32_t)min(tile0 + dma_row[i], Nk - 1) * C::RB + dma_cb[i];
+      __builtin_amdgcn_global_load_lds((gptr_t)(sb + off), (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, 0,
+                                       0);
     }
   };
 
@@ -167,7 +204,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int I = 0; I < 2; ++I) {
         const int key = 8 * vh + 4 * I + ve;
         const int dim = 32 * mb + 16 * (g & 1) + 4 * vq;
-        voff[mb][I] = C::TILE_BYTES + key * C::RB + (((dim >> 3) ^ swz<D>(key)) << 4) + ((dim >> 2) & 1) * 8;
+        voff[mb][I] = key * C::RB + (((dim >> 3) ^ swz<D>(key)) << 4) + ((dim >> 2) & 1) * 8;
       }
   }
 
@@ -175,11 +212,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] = f32x16_t{};
   float m2 = -INFINITY, lsum = 0.f;
+  f32x16_t s0, s1;  // S^T of the current tile, two 32-key blocks
+  u32x4_t pb[4];    // bf16 P^T of the previous tile, four 16-key groups
 
-  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile_compute = [&](const char* st, int tile0, bool need_mask) {
-    const FA_LDS char* kt = (const FA_LDS char*)st;
-    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+  // S_j = K_j Q^T
+  auto qk = [&](const char* kbuf) {
+    const FA_LDS char* kt = (const FA_LDS char*)kbuf;
+    s0 = f32x16_t{};
+    s1 = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       const bf16x8_t a0 = as_bf16x8(lds_load16(kt + koff[ks]));
@@ -187,19 +227,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
     }
-    if (need_mask) {  // wave-uniform: the tile crosses the diagonal or the end of the keys
+  };
+  // O^T += V^T P^T of the previous tile
+  auto pv = [&](const char* vbuf) {
+    const FA_LDS char* vt = (const FA_LDS char*)vbuf;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mb = 0; mb < C::DBLK; ++mb) {
+        const i16x4_t lo = lds_load8_tr16(vt + voff[mb][0] + t * 16 * C::RB);
+        const i16x4_t hi = lds_load8_tr16(vt + voff[mb][1] + t * 16 * C::RB);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[t]), oacc[mb], 0, 0, 0);
+      }
+  };
+  // Pins the MFMA results to the phase that computes them (see the fence in softmax_phase).
+  auto fence_acc = [&]() {
+    asm volatile("" : "+v"(s0), "+v"(s1));
+#pragma unroll
+    for (int mb = 0; mb < C::DBLK; ++mb) asm volatile("" : "+v"(oacc[mb]));
+  };
+  // MFMA phase j (0 < j < n): S_j and O += P_{j-1} V_{j-1} in one scheduling region (K reads
+  // run KA reads ahead of their MFMA, V reads VA MFMAs ahead); in group 0
+  // also the loads of K_{j+1} (a harmless clamped reload when j + 1 = n) and V_j into the free
+  // slots kdst and vdst.
+  auto mfma_phase = [&](auto load_tag, int j, const char* kbuf, const char* vbuf, char* kdst, char* vdst) {
+    if constexpr (decltype(load_tag)::value) {
+      issue(Kh, j + 1, kdst);
+      issue(Vh, j, vdst);
+    }
+    qk(kbuf);
+    pv(vbuf);
+    fence_acc();
+    constexpr int NS = 2 * C::KSTEPS, NP = 4 * C::DBLK;
+    constexpr int KA = FA_KA, VA = FA_VA;
+    __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);
+    static_for<NS - KA>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    static_for<KA>([&](auto I) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (decltype(I)::value < VA) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    });
+    static_for<NP - VA>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, VA, 0);
+  };
+
+  // Softmax phase j: element mask where the tile reaches past the wave's diagonal or the end of
+  // the keys (a tile past the diagonal is masked whole and contributes nothing), running max
+  // raised lazily with the O_acc rescale, P_j = exp2(S_j * scale * log2 e - m) packed to bf16,
+  // row sums into l.
+  auto softmax_phase = [&](int j) {
+    const int tile0 = j * C::BC;
+    if ((tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0)) {
       const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32) : Nk - 1;  // last allowed key of this lane's query
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = tile0 + 16 * (j >> 3) + 8 * hh + (j & 7);
-        if (key > lim) s0[j] = -INFINITY;
-        if (key + 32 > lim) s1[j] = -INFINITY;
+      for (int jj = 0; jj < 16; ++jj) {
+        const int key = tile0 + 16 * (jj >> 3) + 8 * hh + (jj & 7);
+        if (key > lim) s0[jj] = -INFINITY;
+        if (key + 32 > lim) s1[jj] = -INFINITY;
       }
     }
-    // running max (log2 units), raised lazily
-    float mx = fmaxf(s0[0], s1[0]);
+    float mx = max3f(s0[0], s0[1], s1[0]);
+    mx = max3f(mx, s1[1], s0[2]);
 #pragma unroll
-    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
+    for (int jj = 2; jj < 15; ++jj) mx = max3f(mx, s1[jj], s0[jj + 1]);
+    mx = max3f(mx, s1[15], s1[15]);
     mx = max_across_halves(mx) * sl2;
     if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
       const float mnew = fmaxf(m2, mx);
@@ -209,48 +306,102 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] *= alpha;
     }
-    // P^T = exp2(S^T * scale * log2 e - m) in groups of 16 keys; each group, packed to bf16,
-    // is the B operand of one k-step of O^T += V^T P^T.
     const float nm = -m2;
+    float rs = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const f32x16_t& s = (t < 2) ? s0 : s1;
       const int j0 = 8 * (t & 1);
-      u32x4_t pb;
-      float rs = 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float pa = fast_exp2(__builtin_fmaf(s[j0 + 2 * u], sl2, nm));
         const float pc = fast_exp2(__builtin_fmaf(s[j0 + 2 * u + 1], sl2, nm));
         rs += pa + pc;
-        pb[u] = pack_bf16x2(pa, pc);
-      }
-      lsum += rs;
-#pragma unroll
-      for (int mb = 0; mb < C::DBLK; ++mb) {
-        const i16x4_t lo = lds_load8_tr16(kt + voff[mb][0] + t * 16 * C::RB);
-        const i16x4_t hi = lds_load8_tr16(kt + voff[mb][1] + t * 16 * C::RB);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb), oacc[mb], 0, 0, 0);
+        pb[t][u] = pack_bf16x2(pa, pc);
       }
     }
+    lsum += rs;
+    // Keep this phase's vector work in this phase: without the fence the compiler sinks the
+    // exponentials past the barrier, next to their use in the other group's MFMA phase.
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum), "+v"(m2));
   };
 
-  // One step of the tile loop: wait until tile t is in `cur`, start loading tile t + 1 into
-  // `nxt` (everyone has finished reading it: it held tile t - 1), then compute tile t.
-  auto step = [&](int t, const char* cur, char* nxt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t have landed
-    __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1, nxt);
-    const int tile0 = t * C::BC;
-    if (!CAUSAL || tile0 <= q_wave0 + 31)
-      tile_compute(cur, tile0, (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0));
+  // Workgroup barrier between half-periods.  It waits for this wave's LDS reads (the slot may
+  // be refilled next) but not for its tile loads in flight; those are waited for where due.
+  auto bar = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  constexpr std::integral_constant<bool, true> LOAD{};
+  constexpr std::integral_constant<bool, false> NOLOAD{};
 
-  issue_tile(0, stage0);
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, stage0, stage1);
-    if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
+  if (group == 0) issue(Kh, 0, kb0);
+  wait_loads();
+  bar();
+  // Slots by tile parity: K_j in kb[j & 1], V_j in vb[j & 1].  Every wave runs 2n + 3 barriers.
+  if (group == 0) {
+    issue(Kh, 1, kb1);  // h = 0 (K_1 is a clamped reload of K_0 when n = 1)
+    issue(Vh, 0, vb0);
+    qk(kb0);
+    fence_acc();
+    bar();
+    int j = 1;
+    for (; j + 1 < n; j += 2) {
+      softmax_phase(j - 1);  // h = 2j - 1
+      wait_loads();
+      bar();
+      mfma_phase(LOAD, j, kb1, vb0, kb0, vb1);  // h = 2j
+      bar();
+      softmax_phase(j);  // h = 2j + 1
+      wait_loads();
+      bar();
+      mfma_phase(LOAD, j + 1, kb0, vb1, kb1, vb0);  // h = 2j + 2
+      bar();
+    }
+    if (j < n) {  // one more tile (odd j)
+      softmax_phase(j - 1);
+      wait_loads();
+      bar();
+      mfma_phase(LOAD, j, kb1, vb0, kb0, vb1);
+      bar();
+      ++j;
+    }
+    softmax_phase(n - 1);  // h = 2n - 1
+    wait_loads();
+    bar();
+    pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n
+    bar();
+    bar();  // h = 2n + 1: group 1 finishes
+  } else {
+    bar();  // h = 0: idle
+    qk(kb0);  // h = 1
+    fence_acc();
+    bar();
+    int j = 1;
+    for (; j + 1 < n; j += 2) {
+      softmax_phase(j - 1);  // h = 2j
+      bar();
+      mfma_phase(NOLOAD, j, kb1, vb0, kb0, vb1);  // h = 2j + 1
+      bar();
+      softmax_phase(j);  // h = 2j + 2
+      bar();
+      mfma_phase(NOLOAD, j + 1, kb0, vb1, kb1, vb0);  // h = 2j + 3
+      bar();
+    }
+    if (j < n) {
+      softmax_phase(j - 1);
+      bar();
+      mfma_phase(NOLOAD, j, kb1, vb0, kb0, vb1);
+      bar();
+      ++j;
+    }
+    softmax_phase(n - 1);  // h = 2n
+    bar();
+    pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n + 1
+    bar();
   }
 
   // ---- epilogue: O = O_acc / l (RNE to bf16), LSE = (m + log2 l) * ln 2
