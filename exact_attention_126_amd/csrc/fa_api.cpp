@@ -36,7 +36,11 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (!head_fits(Nq, d, dtype) || !head_fits(Nk, d, dtype)) return FA_ERR_SHAPE;
   if (B > kI32Max / H || B * H > kI32Max / ((Nq + 31) / 32)) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_ARG;
-  fa::FwdArgs a{q, k, v, o, lse, (int)B, (int)H, (int)Nq, (int)Nk, (int)d, causal != 0, scale};
+  int dev = 0, num_cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cus <= 0)
+    return FA_ERR_HIP;
+  fa::FwdArgs a{q, k, v, o, lse, (int)B, (int)H, (int)Nq, (int)Nk, (int)d, causal != 0, scale, num_cus};
   return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, stream) : fa::launch_fwd_f32(a, stream));
 }
 

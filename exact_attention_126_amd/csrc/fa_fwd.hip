@@ -89,11 +89,8 @@ struct Bf16Cfg {
 // depend on the value subtracted, Day-21 page §5.2).
 constexpr float kLazyRescale = 8.f;
 
-#ifndef FA_KA
-#define FA_KA 8
-#endif
-#ifndef FA_VA
-#define FA_VA 4
+#ifndef FA_LOOKAHEAD
+#define FA_LOOKAHEAD 8  // MFMAs by which LDS operand reads run ahead
 #endif
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
@@ -118,26 +115,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   p = 2j + 1 softmax phase j: max, lazy rescale, P_j = exp2(S_j - m) (VALU)
 // so on every SIMD one wave feeds the matrix core while the other runs its softmax.  Loads of
 // K_{j+1} and V_j start at half-period 2j and are complete two half-periods later.
+// One query block (batch*head bh, rows qblk*BR ..) of the forward, run by the whole workgroup
+// with the LDS rings kb0/kb1 (K) and vb0/vb1 (V).  The first barrier it executes orders its LDS
+// use after the previous block's; its last barrier is passed only when every wave is done.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int xcd_remap,
-    float sl2) {
+__device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                          float* __restrict__ LSE, int Nq, int Nk, float sl2, int bh, int qblk,
+                                          int n_qblk, char* kb0, char* kb1, char* vb0, char* vb1) {
   using C = Bf16Cfg<D>;
-  // Two-slot rings for K and V tiles.  Separate arrays let the compiler see that reads of one
-  // slot never alias the asynchronous loads into another.
-  __shared__ __attribute__((aligned(1024))) char kb0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kb1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb1[C::TILE_BYTES];
-
-  // ---- workgroup -> (batch*head, query block)
-  int bid = blockIdx.x;
-  if (xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-  int qblk = bid % n_qblk;
-  const int bh = bid / n_qblk;
-  if (CAUSAL) qblk = n_qblk - 1 - qblk;  // most tiles first
-
   const uint16_t* Qh = Q + (int64_t)bh * Nq * D;
   const uint16_t* Kh = K + (int64_t)bh * Nk * D;
   const uint16_t* Vh = V + (int64_t)bh * Nk * D;
@@ -157,9 +143,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = as_bf16x8(gload16(qp + 16 * ks));
   }
 
-  // ---- the workgroup streams n tiles and every wave processes all of them
+  // ---- the workgroup streams n tiles and every wave processes all of them.  Without a mask the
+  // tile order is free, so query blocks of one head start at different tiles (rotation rot):
+  // the workgroups working on a head then stream different parts of its K/V at any moment
+  // instead of all asking the L2 for the same lines.  Step t visits tile (t + rot) mod n; the
+  // extra step t = n (a dummy reload of the free slot) maps to a valid tile too.
   const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR) : Nk;
   const int n = (kv_end + C::BC - 1) / C::BC;
+  const int rot = CAUSAL ? 0 : (int)(((int64_t)qblk * n) / n_qblk);
+  auto tile_of = [&](int t) {
+    const int x = t + rot;
+    return x >= n ? x - n : x;
+  };
 
   // ---- asynchronous global -> LDS tile loads, issued by the four waves of group 0 inside their
   // MFMA phases (their vector units are idle there).  One instruction moves 16 bytes per lane
@@ -175,15 +170,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dma_row[i] = row;
     dma_cb[i] = ((lane % C::CPR) ^ swz<D>(row)) * 16;
   }
+  auto issue_one = [&](const uint16_t* src, int t, char* buf, int i) {
+    const uint32_t off = (uint32_t)min(tile_of(t) * C::BC + dma_row[i], Nk - 1) * C::RB + dma_cb[i];
+    __builtin_amdgcn_global_load_lds((gptr_t)((const char*)src + off),
+                                     (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, 0, 0);
+  };
   auto issue = [&](const uint16_t* src, int t, char* buf) {
-    const int tile0 = t * C::BC;
-    const char* sb = (const char*)src;
 #pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      const uint32_t off = (uint32_t)min(tile0 + dma_row[i], Nk - 1) * C::RB + dma_cb[i];
-      __builtin_amdgcn_global_load_lds((gptr_t)(sb + off), (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, 0,
-                                       0);
-    }
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) issue_one(src, t, buf, i);
   };
 
   // ---- per-lane LDS read offsets
@@ -247,34 +241,55 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int mb = 0; mb < C::DBLK; ++mb) asm volatile("" : "+v"(oacc[mb]));
   };
-  // MFMA phase j (0 < j < n): S_j and O += P_{j-1} V_{j-1} in one scheduling region (K reads
-  // run KA reads ahead of their MFMA, V reads VA MFMAs ahead); in group 0
-  // also the loads of K_{j+1} (a harmless clamped reload when j + 1 = n) and V_j into the free
-  // slots kdst and vdst.
+  // MFMA phase j (0 < j < n): S_j and O += P_{j-1} V_{j-1}, written as an explicit pipeline of
+  // NS + NP slots.  Slot i issues MFMA i (S MFMAs first, then the PV MFMAs), then the LDS reads of
+  // the A operand of MFMA i + L into a rotating set of L + 1 fragment registers, and, when this
+  // wave moves tiles, every DMA_EVERY-th slot one of its global -> LDS loads of K_{j+1} (a
+  // harmless clamped reload when j + 1 = n) and V_j into the free slots kdst and vdst.  Scheduling
+  // barriers between slots keep the compiler from collapsing the read-ahead.
   auto mfma_phase = [&](auto load_tag, int j, const char* kbuf, const char* vbuf, char* kdst, char* vdst) {
-    if constexpr (decltype(load_tag)::value) {
-      issue(Kh, j + 1, kdst);
-      issue(Vh, j, vdst);
-    }
-    qk(kbuf);
-    pv(vbuf);
+    constexpr int NS = 2 * C::KSTEPS, NP = 4 * C::DBLK, N = NS + NP, L = FA_LOOKAHEAD;
+    constexpr int NDMA = decltype(load_tag)::value ? 2 * C::DMA_PER_WAVE : 0;
+    constexpr int DMA_EVERY = N / (NDMA > 0 ? NDMA : 1);
+    const FA_LDS char* kt = (const FA_LDS char*)kbuf;
+    const FA_LDS char* vt = (const FA_LDS char*)vbuf;
+    bf16x8_t frag[L + 1];
+    auto read = [&](auto I) {  // A operand of MFMA I
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < NS) {
+        frag[i % (L + 1)] = as_bf16x8(lds_load16(kt + (i & 1) * 32 * C::RB + koff[i >> 1]));
+      } else {
+        constexpr int t = (i - NS) / C::DBLK, mb = (i - NS) % C::DBLK;
+        const i16x4_t lo = lds_load8_tr16(vt + voff[mb][0] + t * 16 * C::RB);
+        const i16x4_t hi = lds_load8_tr16(vt + voff[mb][1] + t * 16 * C::RB);
+        frag[i % (L + 1)] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    s0 = f32x16_t{};
+    s1 = f32x16_t{};
+    static_for<L>([&](auto I) { read(I); });
+    static_for<N>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < NS) {
+        if constexpr (i & 1)
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % (L + 1)], qf[i >> 1], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % (L + 1)], qf[i >> 1], s0, 0, 0, 0);
+      } else {
+        constexpr int t = (i - NS) / C::DBLK, mb = (i - NS) % C::DBLK;
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % (L + 1)], as_bf16x8(pb[t]), oacc[mb], 0, 0, 0);
+      }
+      if constexpr (i + L < N) read(std::integral_constant<int, i + L>{});
+      if constexpr (NDMA > 0 && i % DMA_EVERY == 0 && i / DMA_EVERY < NDMA) {
+        constexpr int d = i / DMA_EVERY;
+        if constexpr (d < C::DMA_PER_WAVE)
+          issue_one(Kh, j + 1, kdst, d);
+        else
+          issue_one(Vh, j, vdst, d - C::DMA_PER_WAVE);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
     fence_acc();
-    constexpr int NS = 2 * C::KSTEPS, NP = 4 * C::DBLK;
-    constexpr int KA = FA_KA, VA = FA_VA;
-    __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);
-    static_for<NS - KA>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    });
-    static_for<KA>([&](auto I) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (decltype(I)::value < VA) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    });
-    static_for<NP - VA>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    });
-    __builtin_amdgcn_sched_group_barrier(0x008, VA, 0);
   };
 
   // Softmax phase j: element mask where the tile reaches past the wave's diagonal or the end of
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // raised lazily with the O_acc rescale, P_j = exp2(S_j * scale * log2 e - m) packed to bf16,
   // row sums into l.
   auto softmax_phase = [&](int j) {
-    const int tile0 = j * C::BC;
+    const int tile0 = tile_of(j) * C::BC;
     if ((tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0)) {
       const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32) : Nk - 1;  // last allowed key of this lane's query
 #pragma unroll
@@ -425,6 +440,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// Persistent kernel: one workgroup per CU loops over work items.  A causal item is the pair of
+// query blocks q and n_qblk - 1 - q of one head (heaviest first), so every item streams the
+// same number of tiles and the CUs stay balanced; a non-causal item is one query block.  With
+// xcd_split, the items of XCD x (workgroups b with b % 8 == x) are a contiguous range ordered
+// by head, so the 32 CUs of an XCD work on about two heads at a time and share their K/V in
+// that XCD's L2.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int n_items, int items_per_head,
+    int xcd_split, float sl2) {
+  using C = Bf16Cfg<D>;
+  // Two-slot rings for K and V tiles.  Separate arrays let the compiler see that reads of one
+  // slot never alias the asynchronous loads into another.
+  __shared__ __attribute__((aligned(1024))) char kb0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[C::TILE_BYTES];
+
+  const int g = blockIdx.x;
+  int it = g, it_end = n_items, stride = gridDim.x;
+  if (xcd_split) {
+    const int per = n_items >> 3;
+    it = (g & 7) * per + (g >> 3);
+    it_end = (g & 7) * per + per;
+    stride = gridDim.x >> 3;
+  }
+  for (; it < it_end; it += stride) {
+    const int bh = it / items_per_head, r = it % items_per_head;
+    const int qa = CAUSAL ? n_qblk - 1 - r : r;
+    const int cnt = (CAUSAL && r != qa) ? 2 : 1;
+    for (int k = 0; k < cnt; ++k)
+      fwd_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, k == 0 ? qa : r, n_qblk, kb0, kb1, vb0, vb1);
+  }
+}
+
 // ------------------------------------------------------------------ fp32 path
 // Same structure on v_mfma_f32_32x32x2_f32 (no down-conversion anywhere).  k-steps of
 // S^T = K Q^T use the dim order k(t, h) = h*D/2 + t, so each lane reads contiguous float4s;
@@ -546,11 +597,13 @@ template <int D, bool CAUSAL>
 hipError_t launch_bf16_impl(const FwdArgs& a, hipStream_t stream) {
   using C = Bf16Cfg<D>;
   const int n_qblk = (a.Nq + C::BR - 1) / C::BR;
-  const int64_t nblk = (int64_t)a.B * a.H * n_qblk;
-  const int remap = (nblk % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(C::THREADS), 0, stream,
+  const int items_per_head = CAUSAL ? (n_qblk + 1) / 2 : n_qblk;
+  const int64_t n_items = (int64_t)a.B * a.H * items_per_head;
+  const int64_t grid = n_items < a.num_cus ? n_items : a.num_cus;
+  const int xcd_split = (grid % 8 == 0 && n_items % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.Nq, a.Nk, n_qblk, remap, a.scale * kLog2e);
+                     a.Nq, a.Nk, n_qblk, (int)n_items, items_per_head, xcd_split, a.scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ struct FwdArgs {
   int B, H, Nq, Nk, d;
   bool causal;
   float scale;
+  int num_cus;  // compute units of the device the stream runs on (persistent grid size)
 };
 
 struct DecodeSplitArgs {
