@@ -42,12 +42,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// max(a, b, c) in one v_max3_f32.  fmaxf on values the compiler cannot prove canonical (MFMA
-// results) first quiets each input with an extra v_max_f32; scores are never NaN here.
+// max(a, b, c): lowers to one v_maximum3_f32.  Unlike fmaxf (which first quiets each input the
+// compiler cannot prove canonical, such as MFMA results, with an extra instruction) it needs no
+// canonicalisation; it propagates NaN, and scores are never NaN here.  Being visible to the
+// compiler, it also gets the wait states a VALU read of a fresh MFMA result requires.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // Max of a value across the two 32-lane halves of a wave (lane l and lane l ^ 32).
