@@ -28,9 +28,12 @@
 //    V_{j-1} while the other runs the softmax of its tile on the VALU, and the groups swap.
 //    Empty asm statements that take the phase's results as operands keep the compiler from
 //    moving one phase's arithmetic into the next.
-//  * K/V tiles live in two-slot LDS rings and are fetched with global_load_lds_dwordx4, which
+//  * K/V tiles live in two-slot LDS rings and are fetched with buffer_load_dwordx4 ... lds, which
 //    writes HBM/L2 data straight into LDS without passing through VGPRs; the loads are issued
-//    by group 0 inside its MFMA phases and have two half-periods to land.
+//    by group 0 inside its MFMA phases and have two half-periods to land.  The buffer form (not
+//    global_load_lds) matters: the compiler counts only the buffer form's completion on the
+//    vector-memory counter, so its waits for the phase's outstanding LDS reads stay partial
+//    instead of draining every read in flight at each load.
 //  * The running max is raised lazily: the O_acc rescale is skipped unless some row's max grew
 //    by more than 2^8 (the exponentials stay below 256; the result does not depend on the
 //    subtracted value).
@@ -93,8 +96,13 @@ constexpr float kLazyRescale = 8.f;
 #define FA_LOOKAHEAD 8  // MFMAs by which LDS operand reads run ahead
 #endif
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Raw buffer resource over the bytes [base, base + bytes).  Word 3 selects the 32-bit data format:
+// untyped buffer accesses need a non-zero format on this architecture.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -159,9 +167,9 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   // ---- asynchronous global -> LDS tile loads, issued by the four waves of group 0 inside their
   // MFMA phases (their vector units are idle there).  One instruction moves 16 bytes per lane
   // into 1 KiB of consecutive LDS; lane L lands in row L / CPR, slot L % CPR of its rows, so it
-  // fetches the global chunk that the row's swizzle puts in that slot.  Addresses are the head's
-  // base (scalar) plus a 32-bit per-lane byte offset; rows past the end of the keys are clamped
-  // to the last key (their scores are masked).
+  // fetches the global chunk that the row's swizzle puts in that slot.  Addresses are a buffer
+  // resource over the head's K or V plus a 32-bit per-lane byte offset; rows past the end of the
+  // keys are clamped to the last key (their scores are masked).
   const int lw = wave & 3;
   int dma_row[C::DMA_PER_WAVE], dma_cb[C::DMA_PER_WAVE];
 #pragma unroll
@@ -170,12 +178,12 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
     dma_row[i] = row;
     dma_cb[i] = ((lane % C::CPR) ^ swz<D>(row)) * 16;
   }
-  auto issue_one = [&](const uint16_t* src, int t, char* buf, int i) {
+  const __amdgpu_buffer_rsrc_t Kr = raw_rsrc(Kh, Nk * C::RB), Vr = raw_rsrc(Vh, Nk * C::RB);
+  auto issue_one = [&](__amdgpu_buffer_rsrc_t src, int t, char* buf, int i) {
     const uint32_t off = (uint32_t)min(tile_of(t) * C::BC + dma_row[i], Nk - 1) * C::RB + dma_cb[i];
-    __builtin_amdgcn_global_load_lds((gptr_t)((const char*)src + off),
-                                     (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, off, 0, 0, 0);
   };
-  auto issue = [&](const uint16_t* src, int t, char* buf) {
+  auto issue = [&](__amdgpu_buffer_rsrc_t src, int t, char* buf) {
 #pragma unroll
     for (int i = 0; i < C::DMA_PER_WAVE; ++i) issue_one(src, t, buf, i);
   };
@@ -283,9 +291,9 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
       if constexpr (NDMA > 0 && i % DMA_EVERY == 0 && i / DMA_EVERY < NDMA) {
         constexpr int d = i / DMA_EVERY;
         if constexpr (d < C::DMA_PER_WAVE)
-          issue_one(Kh, j + 1, kdst, d);
+          issue_one(Kr, j + 1, kdst, d);
         else
-          issue_one(Vh, j, vdst, d - C::DMA_PER_WAVE);
+          issue_one(Vr, j, vdst, d - C::DMA_PER_WAVE);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -353,13 +361,13 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   constexpr std::integral_constant<bool, true> LOAD{};
   constexpr std::integral_constant<bool, false> NOLOAD{};
 
-  if (group == 0) issue(Kh, 0, kb0);
+  if (group == 0) issue(Kr, 0, kb0);
   wait_loads();
   bar();
   // Slots by tile parity: K_j in kb[j & 1], V_j in vb[j & 1].  Every wave runs 2n + 3 barriers.
   if (group == 0) {
-    issue(Kh, 1, kb1);  // h = 0 (K_1 is a clamped reload of K_0 when n = 1)
-    issue(Vh, 0, vb0);
+    issue(Kr, 1, kb1);  // h = 0 (K_1 is a clamped reload of K_0 when n = 1)
+    issue(Vr, 0, vb0);
     qk(kb0);
     fence_acc();
     bar();
