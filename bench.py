@@ -1,6 +1,7 @@
 """Benchmark of the exact fused attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-baseline on|off] [--copy-calibration]
+                    [--mfma-ceiling on|off]
 
 One step is one pass of the whole path over one batch of synthetic input:
   * the fused causal forward (fa_fwd) on B=8, H=16, Nq=Nk=8192, d=128, bf16, K scaled x2;
@@ -12,7 +13,10 @@ events on the stream it runs on, so per-kernel average durations come from the G
 
 The printed JSON line carries:
   value        forward TFLOP/s = 4*B*H*Nq*Nk*d / 2 (causal) / mean fa_fwd duration
-  roofline     the forward kernel against the dense bf16 MFMA peak (2516.6 TFLOP/s)
+  roofline     the forward kernel against the dense bf16 MFMA peak (2516.6 TFLOP/s); beside it,
+               the sustained matrix-core rate this GPU holds under a long run of back-to-back
+               bf16 MFMAs on N(0,1) operands (libfa_calib.so), which sits below the nominal
+               peak because the engine clock settles under 2.4 GHz
   decode       decode KV-read GB/s (K and V read once) with its own HBM roofline
   cpu_baseline the float64 reference implementation timed on the host cores on a sample
                of the same workload (a reported baseline only)
@@ -133,6 +137,56 @@ def cpu_baseline():
 
 
 # ----------------------------------------------------------------- GPU part
+def sustained_mfma_ceiling(torch, warm_s: float = 0.3, reps: int = 20) -> dict | None:
+    """Sustained dense bf16 MFMA TFLOP/s: one wave per SIMD issues v_mfma_f32_32x32x16_bf16 back to back on
+    seeded N(0,1) bf16 operands (the value distribution of the workload's Q, K, V) for warm_s
+    seconds, then `reps` launches are timed with HIP events; the kernel also reports its shader
+    clock (s_memtime against the 100 MHz s_memrealtime).  None if libfa_calib.so is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "exact_attention_126_amd", "libfa_calib.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.fa_calib_src_bytes.argtypes = [ctypes.c_int]
+    lib.fa_calib_src_bytes.restype = ctypes.c_size_t
+    lib.fa_calib_out_floats.argtypes = [ctypes.c_int]
+    lib.fa_calib_out_floats.restype = ctypes.c_size_t
+    lib.fa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_calib_mfma.restype = ctypes.c_int
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    niter = 40000
+    nb, nf = lib.fa_calib_src_bytes(grid), lib.fa_calib_out_floats(grid)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    src = torch.randn(nb // 2, generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty(nf, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.fa_calib_mfma(src.data_ptr(), nb, out.data_ptr(), nf, clk.data_ptr(), grid, niter, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"fa_calib_mfma failed ({rc})")
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(10):
+            launch()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = grid * 4.0 * 4.0 * niter * 32768.0  # 4 waves per workgroup, 4 * niter MFMAs per wave
+    c = clk.cpu().tolist()
+    ghz = sum(c[2 * i] / (c[2 * i + 1] * 10.0) for i in range(grid)) / grid
+    return {"value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "clock_ghz": round(ghz, 3),
+            "operands": "bf16 N(0,1), seeded", "warm_s": warm_s}
+
+
 def to_device(w, x):
     import numpy as np
     import torch
@@ -145,6 +199,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--mfma-ceiling", choices=["on", "off"], default="on",
+                    help="after the timed steps, measure the sustained bf16 MFMA rate (libfa_calib.so)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference point for HBM counters)")
     args = ap.parse_args()
@@ -229,6 +285,7 @@ def main():
     dec_gbs = kv_bytes / ((ms_split + ms_comb) * 1e-3) / 1e9
     split_gbs = kv_bytes / (ms_split * 1e-3) / 1e9
 
+    ceiling = sustained_mfma_ceiling(torch) if args.mfma_ceiling == "on" else None
     tr_f = read_traffic("fwd_bf16_prefill_b8h16_n8192_d128_causal_hbm_traffic.txt", FWD_SOURCES)
     tr_d = read_traffic("decode_split_b16h32_nk32768_d128_hbm_traffic.txt", DEC_SOURCES)
     line = {
@@ -250,7 +307,9 @@ def main():
         "fwd_ms": round(ms_fwd, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "kernel": "fwd_bf16_kernel<128, causal>",
-                     "traffic": None if tr_f is None else tr_f["bytes"]},
+                     "traffic": None if tr_f is None else tr_f["bytes"],
+                     "sustained_mfma": ceiling,
+                     "frac_of_sustained": None if ceiling is None else round(tflops / ceiling["value"], 4)},
         "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "pct_of_hbm_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
                    "split_ms": round(ms_split, 4), "combine_ms": round(ms_comb, 4),
                    "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -1,4 +1,5 @@
-"""Builds libfa.so (C ABI + gfx950 HIP kernels) in-tree with hipcc.
+"""Builds libfa.so (C ABI + gfx950 HIP kernels) in-tree with hipcc, and libfa_calib.so, the
+sustained matrix-core rate probe that the benchmark reports beside the nominal peak.
 
     python -m exact_attention_126_amd.build [--save-temps]
 
@@ -19,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip"]
+CALIB_LIB = os.path.join(PKG, "libfa_calib.so")
+CALIB_SOURCES = ["calib_mfma.hip"]
 
 
 def hipcc() -> str:
@@ -34,8 +37,8 @@ def flags(save_temps: bool = False):
     return f
 
 
-def build(verbose: bool = False, save_temps: bool = False, out: str = LIB) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+def build(verbose: bool = False, save_temps: bool = False, out: str = LIB, sources=None) -> str:
+    srcs = [os.path.join(CSRC, s) for s in (sources or SOURCES)]
     fd, tmp = tempfile.mkstemp(suffix=".so.tmp", dir=os.path.dirname(out))
     os.close(fd)
     cmd = [hipcc(), *flags(save_temps), "-o", tmp, *srcs]
@@ -59,5 +62,10 @@ def build(verbose: bool = False, save_temps: bool = False, out: str = LIB) -> st
     return out
 
 
+def build_calib(verbose: bool = False) -> str:
+    return build(verbose=verbose, out=CALIB_LIB, sources=CALIB_SOURCES)
+
+
 if __name__ == "__main__":
     build(verbose=True, save_temps="--save-temps" in sys.argv)
+    build_calib(verbose=True)

@@ -118,3 +118,29 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attention(q, q, q)
+
+
+def test_calibration_library_loads_and_validates():
+    """libfa_calib.so (the sustained MFMA-rate probe the benchmark reports beside the nominal
+    peak) loads, sizes its buffers and rejects bad arguments without launching."""
+    path = os.path.join(ROOT, "exact_attention_126_amd", "libfa_calib.so")
+    if not os.path.exists(path):
+        pytest.fail("libfa_calib.so is not built (python -m exact_attention_126_amd.build)")
+    C = ctypes.CDLL(path)
+    C.fa_calib_src_bytes.argtypes = [ctypes.c_int]
+    C.fa_calib_src_bytes.restype = ctypes.c_size_t
+    C.fa_calib_out_floats.argtypes = [ctypes.c_int]
+    C.fa_calib_out_floats.restype = ctypes.c_size_t
+    C.fa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    C.fa_calib_mfma.restype = ctypes.c_int
+    assert C.fa_calib_src_bytes(256) == 256 * 8 * 64 * 16
+    assert C.fa_calib_out_floats(256) == 256 * 256
+    assert C.fa_calib_src_bytes(0) == 0
+    nb, nf = C.fa_calib_src_bytes(4), C.fa_calib_out_floats(4)
+    assert C.fa_calib_mfma(None, nb, P, nf, P, 4, 8, None) == -1         # null operand buffer
+    assert C.fa_calib_mfma(P, nb - 16, P, nf, P, 4, 8, None) == -1       # operand buffer too small
+    assert C.fa_calib_mfma(P, nb, P, nf - 1, P, 4, 8, None) == -1        # output buffer too small
+    assert C.fa_calib_mfma(P_MIS, nb, P, nf, P, 4, 8, None) == -1        # misaligned operands
+    assert C.fa_calib_mfma(P, nb, P, nf, P, 4, 6, None) == -1            # niter not a multiple of 4
+    assert C.fa_calib_mfma(P, nb, P, nf, P, 0, 8, None) == -1            # empty grid
