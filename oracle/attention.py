@@ -3,7 +3,10 @@
 What is computed (Day-21 page §3.1 "standard implementation data flow" and §5.1;
 M4-047 card §3):
     S   = scale * Q K^T                       (Nq x Nk; scale = 1/sqrt(d) in the pages)
-    S_ij = -inf where j > i                   (causal mask, only when requested)
+    S_ij = -inf where j > i + diag            (causal mask, only when requested; diag = 0 is
+                                               the usual top-left diagonal, diag = Nk - Nq puts
+                                               the last query on the last key: a chunk of new
+                                               queries appended to a KV cache)
     m_i = max_j S_ij                          (pass 1 of the safe softmax, Day-21 §5.1)
     e_ij = exp(S_ij - m_i), l_i = sum_j e_ij  (pass 2)
     P   = e / l,  O = P V
@@ -12,6 +15,11 @@ M4-047 card §3):
 
 Rows may be processed in chunks to bound memory, but every chunk spans all keys,
 so each row's two passes see the whole row.  Nothing here uses the online recurrence.
+
+Grouped K/V heads (GQA: several query heads share one K/V head; the Day-21 page's FAQ Q5 lists
+it among the techniques that matter at decode, where reading the KV cache is the bottleneck):
+with H query heads and H_kv K/V heads, H_kv dividing H, query head h reads K/V head
+h // (H / H_kv).  H_kv = H is ordinary multi-head attention.
 
 Split-KV decode (Q31 answer, follow-up 3: split K/V into chunks processed in parallel,
 then merge; the merge rescales with exp(m_block - m_global), follow-up 2):
@@ -50,11 +58,13 @@ def softmax_two_pass(s: np.ndarray):
     return e / l, m[..., 0], l[..., 0]
 
 
-def attention_head(q, k, v, scale: float, causal: bool = False, rows=None, row_chunk: int = 1024):
+def attention_head(q, k, v, scale: float, causal: bool = False, rows=None, row_chunk: int = 1024,
+                   diag: int = 0):
     """One head. q [Nq, d], k and v [Nk, d] -> (O [n, d], LSE [n]) in float64.
 
     rows: optional increasing 1-D array of query row indices to compute (the causal
-    mask uses the true row index); default all rows.
+    mask uses the true row index); default all rows.  causal: key j is visible to query
+    row i iff j <= i + diag.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
@@ -64,23 +74,29 @@ def attention_head(q, k, v, scale: float, causal: bool = False, rows=None, row_c
         r = rows[c0:c0 + row_chunk]
         s = float(scale) * (q[r] @ k.T)
         if causal:
-            s = np.where(np.arange(k.shape[0])[None, :] > r[:, None], -np.inf, s)
+            s = np.where(np.arange(k.shape[0])[None, :] > r[:, None] + diag, -np.inf, s)
         p, m, l = softmax_two_pass(s)
         o[c0:c0 + len(r)] = p @ v
         lse[c0:c0 + len(r)] = m + np.log(l)
     return o, lse
 
 
-def attention(q, k, v, scale: float, causal: bool = False, row_chunk: int = 1024):
-    """[B, H, Nq, d] x [B, H, Nk, d] x [B, H, Nk, d] -> (O [B, H, Nq, d], LSE [B, H, Nq]) float64."""
-    q = np.asarray(q)
+def attention(q, k, v, scale: float, causal: bool = False, row_chunk: int = 1024, diag: int = 0):
+    """[B, H, Nq, d] x [B, H_kv, Nk, d] x [B, H_kv, Nk, d] -> (O [B, H, Nq, d], LSE [B, H, Nq]) float64.
+
+    H_kv must divide H; query head h attends with K/V head h // (H // H_kv)."""
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     B, H, Nq, _ = q.shape
-    o = np.empty(q.shape[:3] + (np.asarray(v).shape[-1],), dtype=np.float64)
+    H_kv = k.shape[1]
+    if H % H_kv != 0 or v.shape[1] != H_kv:
+        raise ValueError(f"H_kv = {H_kv} K/V heads do not divide H = {H} query heads")
+    group = H // H_kv
+    o = np.empty(q.shape[:3] + (v.shape[-1],), dtype=np.float64)
     lse = np.empty((B, H, Nq), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], scale, causal,
-                                                row_chunk=row_chunk)
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h // group], v[b, h // group], scale, causal,
+                                                row_chunk=row_chunk, diag=diag)
     return o, lse
 
 
