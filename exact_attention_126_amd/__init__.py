@@ -19,10 +19,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F32 = 1
+FA_MASK_NONE = 0
+FA_MASK_CAUSAL = 1
+FA_MASK_CAUSAL_BOTTOM_RIGHT = 2
+MASKS = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "causal_bottom_right": FA_MASK_CAUSAL_BOTTOM_RIGHT}
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE", 4: "FA_ERR_UNSUPPORTED",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
-EXPORTED = ["fa_fwd", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_combine", "fa_status_string"]
+EXPORTED = ["fa_fwd", "fa_fwd_ex", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_split_ex",
+            "fa_decode_combine", "fa_status_string"]
 
 _lib = None
 
@@ -43,6 +48,10 @@ def lib() -> ctypes.CDLL:
         i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
         L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, vp]
         L.fa_fwd.restype = i32
+        L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
+        L.fa_fwd_ex.restype = i32
+        L.fa_decode_split_ex.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+        L.fa_decode_split_ex.restype = i32
         L.fa_decode_workspace_bytes.argtypes = [i64, i64, i64, i32]
         L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.fa_decode_split.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, f32, i32, i32, vp]
@@ -86,6 +95,18 @@ def _check(t: torch.Tensor, name: str, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_shapes(q, k, v, o=None, lse=None, same_heads: bool = True):
+    """The library sees only pointers and sizes, so the sizes it is given must describe the tensors."""
+    if q.dim() != 4 or k.dim() != 4 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}: need [B,H,N,d] and v like k")
+    if k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3] or (same_heads and k.shape[1] != q.shape[1]):
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch, heads or head dim")
+    if o is not None and tuple(o.shape) != tuple(q.shape):
+        raise ValueError(f"o {tuple(o.shape)} must have the shape of q {tuple(q.shape)}")
+    if lse is not None and tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError(f"lse {tuple(lse.shape)} must be {tuple(q.shape[:3])}")
+
+
 def _raise(status: int, where: str):
     if status != FA_OK:
         raise FAError(status, where)
@@ -96,6 +117,7 @@ def fa_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = None, st
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _check(t, n, q.dtype)
     _check(lse, "lse", torch.float32)
+    _check_shapes(q, k, v, o, lse)
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if scale is None:
@@ -103,6 +125,23 @@ def fa_fwd(q, k, v, o, lse, causal: bool = False, scale: float | None = None, st
     st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)),
                       float(scale), _dtype_code(q), _stream(stream))
     _raise(st, "fa_fwd")
+
+
+def fa_fwd_ex(q, k, v, o, lse, mask=FA_MASK_NONE, scale: float | None = None, stream=None) -> None:
+    """Forward with grouped K/V heads (k, v [B,H_kv,Nk,d], H_kv dividing H) and a causal alignment
+    (FA_MASK_NONE, FA_MASK_CAUSAL top-left, FA_MASK_CAUSAL_BOTTOM_RIGHT; or their MASKS names)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, n, q.dtype)
+    _check(lse, "lse", torch.float32)
+    _check_shapes(q, k, v, o, lse, same_heads=False)
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    m = MASKS[mask] if isinstance(mask, str) else int(mask)
+    st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, H_kv, Nq, Nk, d, m, float(scale),
+                         _dtype_code(q), _stream(stream))
+    _raise(st, "fa_fwd_ex")
 
 
 def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
@@ -114,6 +153,9 @@ def fa_decode_split(q, k, v, workspace, num_splits: int, scale: float | None = N
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, q.dtype)
     _check(workspace, "workspace")
+    _check_shapes(q, k, v)
+    if q.shape[2] != 1:
+        raise ValueError(f"decode takes one query token per head, q is {tuple(q.shape)}")
     B, H, _, d = q.shape
     Nk = k.shape[2]
     if scale is None:
@@ -121,6 +163,24 @@ def fa_decode_split(q, k, v, workspace, num_splits: int, scale: float | None = N
     st = lib().fa_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                B, H, Nk, d, float(scale), int(num_splits), _dtype_code(q), _stream(stream))
     _raise(st, "fa_decode_split")
+
+
+def fa_decode_split_ex(q, k, v, workspace, num_splits: int, scale: float | None = None, stream=None) -> None:
+    """Per-split decode partials with grouped K/V heads: q [B,H,1,d], k/v [B,H_kv,Nk,d]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    _check(workspace, "workspace")
+    _check_shapes(q, k, v, same_heads=False)
+    if q.shape[2] != 1:
+        raise ValueError(f"decode takes one query token per head, q is {tuple(q.shape)}")
+    B, H, _, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_decode_split_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), B, H, H_kv, Nk, d, float(scale),
+                                  int(num_splits), _dtype_code(q), _stream(stream))
+    _raise(st, "fa_decode_split_ex")
 
 
 def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None) -> None:
@@ -135,12 +195,17 @@ def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None) -> None:
 
 
 # ---- conveniences that allocate the outputs with torch and call the entry points above
-def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
-    """(o, lse) = attention(q, k, v): allocates the outputs and calls fa_fwd."""
+def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=None, mask=None):
+    """(o, lse) = attention(q, k, v): allocates the outputs and calls fa_fwd, or fa_fwd_ex when
+    k/v have fewer heads than q or a mask (fa_mask_t value or MASKS name) is given."""
     B, H, Nq, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, causal, scale, stream)
+    if mask is None and k.shape[1] == H:
+        fa_fwd(q, k, v, o, lse, causal, scale, stream)
+    else:
+        fa_fwd_ex(q, k, v, o, lse, (FA_MASK_CAUSAL if causal else FA_MASK_NONE) if mask is None else mask, scale,
+                  stream)
     return o, lse
 
 
@@ -150,12 +215,16 @@ def decode_workspace(q, num_splits: int):
 
 
 def decode(q, k, v, num_splits: int, scale: float | None = None, workspace=None, stream=None):
-    """(o, lse) of one-token decode: fa_decode_split then fa_decode_combine on the same stream."""
+    """(o, lse) of one-token decode: fa_decode_split (fa_decode_split_ex when k/v have fewer heads
+    than q) then fa_decode_combine on the same stream."""
     B, H, _, d = q.shape
     if workspace is None:
         workspace = decode_workspace(q, num_splits)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
-    fa_decode_split(q, k, v, workspace, num_splits, scale, stream)
+    if k.shape[1] == H:
+        fa_decode_split(q, k, v, workspace, num_splits, scale, stream)
+    else:
+        fa_decode_split_ex(q, k, v, workspace, num_splits, scale, stream)
     fa_decode_combine(workspace, o, lse, num_splits, stream)
     return o, lse

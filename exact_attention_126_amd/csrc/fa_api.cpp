@@ -20,19 +20,18 @@ bool head_fits(int64_t n, int64_t d, fa_dtype_t t) { return n <= kI32Max / (d * 
 
 fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                   int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, fa_dtype_t dtype,
-                   hipStream_t stream) {
+// The forward behind fa_fwd and fa_fwd_ex; `mask` already known to be one of the three values.
+// square_causal: fa_fwd's contract, a causal mask only with Nq == Nk.
+fa_status_t forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                    int64_t H_kv, int64_t Nq, int64_t Nk, int64_t d, fa_mask_t mask, bool square_causal,
+                    float scale, fa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!dtype_ok(dtype) || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_ALIGN;
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
-  if (causal && Nq != Nk) return FA_ERR_SHAPE;
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Nq <= 0 || Nk <= 0 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (mask == FA_MASK_CAUSAL_BOTTOM_RIGHT && Nk < Nq) return FA_ERR_SHAPE;  // a row would see no key
+  if (square_causal && mask != FA_MASK_NONE && Nq != Nk) return FA_ERR_SHAPE;
   if (!head_fits(Nq, d, dtype) || !head_fits(Nk, d, dtype)) return FA_ERR_SHAPE;
   if (B > kI32Max / H || B * H > kI32Max / ((Nq + 31) / 32)) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_ARG;
@@ -40,8 +39,48 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cus <= 0)
     return FA_ERR_HIP;
-  fa::FwdArgs a{q, k, v, o, lse, (int)B, (int)H, (int)Nq, (int)Nk, (int)d, causal != 0, scale, num_cus};
+  const bool causal = mask != FA_MASK_NONE;
+  const int diag = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT ? (int)(Nk - Nq) : 0;
+  fa::FwdArgs a{q, k, v, o, lse, (int)B, (int)H, (int)Nq, (int)Nk, (int)d, (int)H_kv, causal, diag, scale, num_cus};
   return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, stream) : fa::launch_fwd_f32(a, stream));
+}
+
+// The split step behind fa_decode_split and fa_decode_split_ex.
+fa_status_t decode_split(const void* q, const void* k, const void* v, void* workspace, size_t workspace_bytes,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t Nk, int64_t d, float scale, int num_splits,
+                         fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !workspace) return FA_ERR_NULL;
+  if (!dtype_ok(dtype) || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(workspace, 16)) return FA_ERR_ALIGN;
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Nk <= 0 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (!head_fits(Nk, d, dtype) || B > kI32Max / H) return FA_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > Nk || !scale_ok(scale)) return FA_ERR_ARG;
+  if (B * H > kI32Max / num_splits) return FA_ERR_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  float* o_part = static_cast<float*>(workspace);
+  float* ml = o_part + (size_t)(B * H * num_splits) * (size_t)d;
+  fa::DecodeSplitArgs a{q, k, v, o_part, ml, (int)B, (int)H, (int)Nk, (int)d, num_splits, (int)H_kv, scale};
+  return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_decode_split_bf16(a, stream)
+                                         : fa::launch_decode_split_f32(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, fa_dtype_t dtype,
+                   hipStream_t stream) {
+  return forward(q, k, v, o, lse, B, H, H, Nq, Nk, d, causal ? FA_MASK_CAUSAL : FA_MASK_NONE, true, scale, dtype,
+                 stream);
+}
+
+fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                      int64_t H_kv, int64_t Nq, int64_t Nk, int64_t d, fa_mask_t mask, float scale, fa_dtype_t dtype,
+                      hipStream_t stream) {
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_CAUSAL_BOTTOM_RIGHT) return FA_ERR_ARG;
+  return forward(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, mask, false, scale, dtype, stream);
 }
 
 size_t fa_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int num_splits) {
@@ -53,20 +92,13 @@ size_t fa_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int num_splits
 fa_status_t fa_decode_split(const void* q, const void* k, const void* v, void* workspace, size_t workspace_bytes,
                             int64_t B, int64_t H, int64_t Nk, int64_t d, float scale, int num_splits,
                             fa_dtype_t dtype, hipStream_t stream) {
-  if (!q || !k || !v || !workspace) return FA_ERR_NULL;
-  if (!dtype_ok(dtype) || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(workspace, 16)) return FA_ERR_ALIGN;
-  if (B <= 0 || H <= 0 || Nk <= 0) return FA_ERR_SHAPE;
-  if (!head_fits(Nk, d, dtype) || B > kI32Max / H) return FA_ERR_SHAPE;
-  if (num_splits < 1 || num_splits > Nk || !scale_ok(scale)) return FA_ERR_ARG;
-  if (B * H > kI32Max / num_splits) return FA_ERR_SHAPE;
-  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
-  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
-  float* o_part = static_cast<float*>(workspace);
-  float* ml = o_part + (size_t)(B * H * num_splits) * (size_t)d;
-  fa::DecodeSplitArgs a{q, k, v, o_part, ml, (int)B, (int)H, (int)Nk, (int)d, num_splits, scale};
-  return from_hip(dtype == FA_DTYPE_BF16 ? fa::launch_decode_split_bf16(a, stream)
-                                         : fa::launch_decode_split_f32(a, stream));
+  return decode_split(q, k, v, workspace, workspace_bytes, B, H, H, Nk, d, scale, num_splits, dtype, stream);
+}
+
+fa_status_t fa_decode_split_ex(const void* q, const void* k, const void* v, void* workspace, size_t workspace_bytes,
+                               int64_t B, int64_t H, int64_t H_kv, int64_t Nk, int64_t d, float scale, int num_splits,
+                               fa_dtype_t dtype, hipStream_t stream) {
+  return decode_split(q, k, v, workspace, workspace_bytes, B, H, H_kv, Nk, d, scale, num_splits, dtype, stream);
 }
 
 fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse, int64_t B,
@@ -91,11 +123,14 @@ const char* fa_status_string(fa_status_t s) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_ALIGN: return "pointer misaligned (tensors need 16 bytes, lse 4 bytes)";
-    case FA_ERR_SHAPE: return "invalid shape (size <= 0, causal with Nq != Nk, or beyond index limits)";
+    case FA_ERR_SHAPE:
+      return "invalid shape (size <= 0, H_kv not dividing H, a causal alignment some row sees no key under, "
+             "or beyond index limits)";
     case FA_ERR_UNSUPPORTED: return "unsupported head dim (64 or 128) or dtype";
     case FA_ERR_WORKSPACE: return "decode workspace too small";
     case FA_ERR_HIP: return "HIP runtime error at launch";
-    case FA_ERR_ARG: return "invalid scalar argument (scale must be finite and > 0; 1 <= num_splits <= Nk)";
+    case FA_ERR_ARG:
+      return "invalid scalar argument (scale must be finite and > 0; 1 <= num_splits <= Nk; known mask)";
   }
   return "unknown status";
 }

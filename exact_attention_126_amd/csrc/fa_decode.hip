@@ -67,7 +67,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, float* __restrict__ Opart,
                                                            float* __restrict__ ML, int Nk, int S, int chunk,
-                                                           float sl2) {
+                                                           float sl2, int H, int group) {
   constexpr int EPL = Elt<T>::PER16;  // elements per lane per key row
   constexpr int LPK = D / EPL;        // lanes per key row
   constexpr int KPW = 64 / LPK;       // key rows per wave per step
@@ -85,8 +85,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
 
   float qv[EPL];
   Elt<T>::widen(gload16(Q + (int64_t)bh * D + li * EPL), qv);
-  const T* Kh = K + (int64_t)bh * Nk * D + li * EPL;
-  const T* Vh = V + (int64_t)bh * Nk * D + li * EPL;
+  const int kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
+  const T* Kh = K + (int64_t)kvh * Nk * D + li * EPL;
+  const T* Vh = V + (int64_t)kvh * Nk * D + li * EPL;
 
   float m = -INFINITY, l = 0.f, acc[EPL];
 #pragma unroll
@@ -196,10 +197,12 @@ hipError_t split_impl(const DecodeSplitArgs& a, hipStream_t stream) {
   const float sl2 = a.scale * kLog2e;
   if (a.d == 128)
     hipLaunchKernelGGL((decode_split_kernel<T, 128>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T*)a.q,
-                       (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2);
+                       (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2, a.H,
+                       a.H / a.H_kv);
   else
     hipLaunchKernelGGL((decode_split_kernel<T, 64>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T*)a.q,
-                       (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2);
+                       (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2, a.H,
+                       a.H / a.H_kv);
   return hipGetLastError();
 }
 

@@ -129,12 +129,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                                          float* __restrict__ LSE, int Nq, int Nk, float sl2, int bh, int qblk,
-                                          int n_qblk, char* kb0, char* kb1, char* vb0, char* vb1) {
+                                          float* __restrict__ LSE, int Nq, int Nk, float sl2, int bh, int kvh,
+                                          int diag, int qblk, int n_qblk, char* kb0, char* kb1, char* vb0,
+                                          char* vb1) {
   using C = Bf16Cfg<D>;
   const uint16_t* Qh = Q + (int64_t)bh * Nq * D;
-  const uint16_t* Kh = K + (int64_t)bh * Nk * D;
-  const uint16_t* Vh = V + (int64_t)bh * Nk * D;
+  const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
+  const uint16_t* Vh = V + (int64_t)kvh * Nk * D;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -156,7 +157,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   // the workgroups working on a head then stream different parts of its K/V at any moment
   // instead of all asking the L2 for the same lines.  Step t visits tile (t + rot) mod n; the
   // extra step t = n (a dummy reload of the free slot) maps to a valid tile too.
-  const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR) : Nk;
+  const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR + diag) : Nk;
   const int n = (kv_end + C::BC - 1) / C::BC;
   const int rot = CAUSAL ? 0 : (int)(((int64_t)qblk * n) / n_qblk);
   auto tile_of = [&](int t) {
@@ -306,8 +307,8 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   // row sums into l.
   auto softmax_phase = [&](int j) {
     const int tile0 = tile_of(j) * C::BC;
-    if ((tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0)) {
-      const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32) : Nk - 1;  // last allowed key of this lane's query
+    if ((tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag)) {
+      const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32 + diag) : Nk - 1;  // last key this lane's query sees
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int key = tile0 + 16 * (jj >> 3) + 8 * hh + (jj & 7);
@@ -458,7 +459,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int n_items, int items_per_head,
-    int xcd_split, float sl2) {
+    int xcd_split, float sl2, int H, int group, int diag) {
   using C = Bf16Cfg<D>;
   // Two-slot rings for K and V tiles.  Separate arrays let the compiler see that reads of one
   // slot never alias the asynchronous loads into another.
@@ -477,10 +478,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   for (; it < it_end; it += stride) {
     const int bh = it / items_per_head, r = it % items_per_head;
+    const int kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
     const int qa = CAUSAL ? n_qblk - 1 - r : r;
     const int cnt = (CAUSAL && r != qa) ? 2 : 1;
     for (int k = 0; k < cnt; ++k)
-      fwd_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, k == 0 ? qa : r, n_qblk, kb0, kb1, vb0, vb1);
+      fwd_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, k == 0 ? qa : r, n_qblk, kb0, kb1, vb0,
+                           vb1);
   }
 }
 
@@ -493,7 +496,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int Nq, int Nk, int n_qblk,
-                                                      float sl2) {
+                                                      float sl2, int H, int group, int diag) {
   constexpr int BR = 128, BC = 32, RS = D + 4, HALF = D / 2, DBLK = D / 32;
   constexpr int TILE_FLOATS = BC * RS;
   constexpr int CH_PER_ROW = D / 4;
@@ -504,9 +507,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   int qblk = blockIdx.x % n_qblk;
   const int bh = blockIdx.x / n_qblk;
   if (CAUSAL) qblk = n_qblk - 1 - qblk;
+  const int kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
   const float* Qh = Q + (int64_t)bh * Nq * D;
-  const float* Kh = K + (int64_t)bh * Nk * D;
-  const float* Vh = V + (int64_t)bh * Nk * D;
+  const float* Kh = K + (int64_t)kvh * Nk * D;
+  const float* Vh = V + (int64_t)kvh * Nk * D;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int q_wave0 = qblk * BR + wave * 32;
 
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       qf[i] = x[0]; qf[i + 1] = x[1]; qf[i + 2] = x[2]; qf[i + 3] = x[3];
     }
   }
-  const int kv_end = CAUSAL ? min(Nk, qblk * BR + BR) : Nk;
+  const int kv_end = CAUSAL ? min(Nk, qblk * BR + BR + diag) : Nk;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
   f32x16_t oacc[DBLK];
@@ -538,7 +542,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       *(f32x4_t*)&vt[r * RS + 4 * c] = *(const f32x4_t*)(Vh + (int64_t)row * D + 4 * c);
     }
     __syncthreads();
-    if (CAUSAL && tile0 > q_wave0 + 31) continue;
+    if (CAUSAL && tile0 > q_wave0 + 31 + diag) continue;
     f32x16_t s = f32x16_t{};
     const float* kr = &kt[l32 * RS + hh * HALF];
 #pragma unroll
@@ -549,13 +553,13 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], qf[i + 2], s, 0, 0, 0);
       s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], qf[i + 3], s, 0, 0, 0);
     }
-    const bool need_mask = (tile0 + BC > Nk) || (CAUSAL && tile0 + BC - 1 > q_wave0);
+    const bool need_mask = (tile0 + BC > Nk) || (CAUSAL && tile0 + BC - 1 > q_wave0 + diag);
     if (need_mask) {
       const int q = q_wave0 + l32;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = tile0 + 8 * (j >> 2) + 4 * hh + (j & 3);
-        if (key >= Nk || (CAUSAL && key > q)) s[j] = -INFINITY;
+        if (key >= Nk || (CAUSAL && key > q + diag)) s[j] = -INFINITY;
       }
     }
     float mx = s[0];
@@ -611,7 +615,8 @@ hipError_t launch_bf16_impl(const FwdArgs& a, hipStream_t stream) {
   const int xcd_split = (grid % 8 == 0 && n_items % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.Nq, a.Nk, n_qblk, (int)n_items, items_per_head, xcd_split, a.scale * kLog2e);
+                     a.Nq, a.Nk, n_qblk, (int)n_items, items_per_head, xcd_split, a.scale * kLog2e, a.H,
+                     a.H / a.H_kv, a.diag);
   return hipGetLastError();
 }
 
@@ -621,7 +626,7 @@ hipError_t launch_f32_impl(const FwdArgs& a, hipStream_t stream) {
   const int64_t nblk = (int64_t)a.B * a.H * n_qblk;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(256), 0, stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.Nq, a.Nk,
-                     n_qblk, a.scale * kLog2e);
+                     n_qblk, a.scale * kLog2e, a.H, a.H / a.H_kv, a.diag);
   return hipGetLastError();
 }
 

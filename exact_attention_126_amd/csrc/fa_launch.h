@@ -14,7 +14,9 @@ struct FwdArgs {
   void* o;
   float* lse;
   int B, H, Nq, Nk, d;
+  int H_kv;    // K/V heads; divides H, query head h reads K/V head h / (H / H_kv)
   bool causal;
+  int diag;    // causal: key j visible to query i iff j <= i + diag (0 top-left, Nk - Nq bottom-right)
   float scale;
   int num_cus;  // compute units of the device the stream runs on (persistent grid size)
 };
@@ -26,6 +28,7 @@ struct DecodeSplitArgs {
   float* o_part;  // [B][H][S][d]
   float* ml;      // [B][H][S][2]
   int B, H, Nk, d, num_splits;
+  int H_kv;       // K/V heads; divides H, query head h reads K/V head h / (H / H_kv)
   float scale;
 };
 

@@ -40,15 +40,27 @@ typedef struct ihipStream_t* hipStream_t;
 
 typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype_t;
 
+/* Causal alignment for fa_fwd_ex.  Query row i (0-based) may attend to key j iff
+ *   FA_MASK_NONE:                 always;
+ *   FA_MASK_CAUSAL:               j <= i                (top-left diagonal, any Nq and Nk);
+ *   FA_MASK_CAUSAL_BOTTOM_RIGHT:  j <= i + (Nk - Nq)    (the last query sees every key: Nq new
+ *                                 tokens appended to a KV cache of Nk - Nq earlier ones, the
+ *                                 prefill-against-a-cache case of the Day-21 page §9; needs
+ *                                 Nk >= Nq so that every row sees at least one key).
+ * The pages do not fix an alignment for Nq != Nk; both are offered, and with Nq == Nk they agree. */
+typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_CAUSAL_BOTTOM_RIGHT = 2 } fa_mask_t;
+
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
   FA_ERR_ALIGN = 2,       /* q/k/v/o/workspace not 16-byte aligned, or lse not 4-byte aligned */
-  FA_ERR_SHAPE = 3,       /* a size <= 0, causal with Nq != Nk, or sizes beyond the index limits */
+  FA_ERR_SHAPE = 3,       /* a size <= 0, H_kv not dividing H, causal with Nq != Nk (fa_fwd) or
+                             bottom-right with Nk < Nq, or sizes beyond the index limits */
   FA_ERR_UNSUPPORTED = 4, /* d not in {64, 128}, or unknown dtype */
   FA_ERR_WORKSPACE = 5,   /* decode workspace smaller than fa_decode_workspace_bytes() */
   FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
-  FA_ERR_ARG = 7          /* scale not finite and > 0, or num_splits outside [1, Nk] */
+  FA_ERR_ARG = 7          /* scale not finite and > 0, num_splits outside [1, Nk], or an unknown
+                             fa_mask_t */
 } fa_status_t;
 
 /*
@@ -62,6 +74,20 @@ typedef enum {
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                    int causal, float scale, fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Fused attention forward with grouped K/V heads and a choice of causal alignment.
+ *   q [B,H,Nq,d], k and v [B,H_kv,Nk,d]  (in), o [B,H,Nq,d] and lse [B,H,Nq] float32 (out).
+ *   H_kv must divide H; query head h reads K/V head h / (H / H_kv) (grouped-query attention,
+ *   which the Day-21 page's FAQ Q5 lists among the techniques that matter once reading K/V
+ *   dominates; H_kv == H is multi-head attention, H_kv == 1 multi-query attention).
+ *   mask: see fa_mask_t.  Everything else (dtypes, layouts, precision, limits, errors) is as
+ *   for fa_fwd, which equals fa_fwd_ex with H_kv = H and mask = causal ? FA_MASK_CAUSAL :
+ *   FA_MASK_NONE (fa_fwd additionally rejects causal with Nq != Nk).
+ */
+fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t H_kv, int64_t Nq, int64_t Nk, int64_t d,
+                      fa_mask_t mask, float scale, fa_dtype_t dtype, hipStream_t stream);
 
 /*
  * Split-KV decode (one query token per (b, h) against a KV cache): the keys are split into
@@ -84,6 +110,18 @@ fa_status_t fa_decode_split(const void* q, const void* k, const void* v,
                             void* workspace, size_t workspace_bytes,
                             int64_t B, int64_t H, int64_t Nk, int64_t d, float scale,
                             int num_splits, fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Split step of decode with grouped K/V heads: q [B,H,1,d], k and v [B,H_kv,Nk,d], H_kv
+ * dividing H; query head h reads K/V head h / (H / H_kv) (see fa_fwd_ex).  The workspace, its
+ * size (per query head: fa_decode_workspace_bytes(B, H, d, num_splits)), the merge
+ * (fa_decode_combine, unchanged) and the errors are as for fa_decode_split, which equals
+ * fa_decode_split_ex with H_kv = H.
+ */
+fa_status_t fa_decode_split_ex(const void* q, const void* k, const void* v,
+                               void* workspace, size_t workspace_bytes,
+                               int64_t B, int64_t H, int64_t H_kv, int64_t Nk, int64_t d, float scale,
+                               int num_splits, fa_dtype_t dtype, hipStream_t stream);
 
 /* Merges the workspace into o [B,H,1,d] (dtype) and lse [B,H,1] float32. */
 fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse,

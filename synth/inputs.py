@@ -77,17 +77,19 @@ def head_block_f32(w: Workload, which: str, b: int, h: int) -> np.ndarray:
 
 
 def make_tensor(w: Workload, which: str, threads: int | None = None) -> np.ndarray:
-    """Full [B, H, rows, d] tensor in storage form, heads drawn in parallel."""
+    """Full [B, heads, rows, d] tensor in storage form (heads = H for Q, the K/V head count for
+    K and V), heads drawn in parallel."""
     rows = w.Nq if which == "q" else w.Nk
-    out = np.empty((w.B, w.H, rows, w.d), dtype=np.uint16 if w.dtype == "bf16" else np.float32)
+    heads = w.H if which == "q" else w.kv_heads
+    out = np.empty((w.B, heads, rows, w.d), dtype=np.uint16 if w.dtype == "bf16" else np.float32)
     threads = threads or min(16, len(os.sched_getaffinity(0)))
 
     def fill(bh):
-        b, h = divmod(bh, w.H)
+        b, h = divmod(bh, heads)
         out[b, h] = head_block(w, which, b, h)
 
     with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(fill, range(w.B * w.H)))
+        list(ex.map(fill, range(w.B * heads)))
     return out
 
 

@@ -36,6 +36,16 @@ class Workload:
     k_rule: tuple = ("none",)
     num_splits: int = 0  # > 0: decode workload, split-KV into this many partitions
     description: str = ""
+    H_kv: int = 0  # K/V heads (0: H); query head h reads K/V head h // (H // H_kv)
+    causal_align: str = "top_left"  # or "bottom_right": key j visible to row i iff j <= i + Nk - Nq
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
+
+    @property
+    def diag(self) -> int:
+        return self.Nk - self.Nq if (self.causal and self.causal_align == "bottom_right") else 0
 
     @property
     def scale(self) -> float:
@@ -71,6 +81,15 @@ WORKLOADS = {
             "decode_b16h32_nk32768_d128", B=16, H=32, Nq=1, Nk=32768, d=128, dtype="bf16",
             causal=False, seed=5000, num_splits=64,
             description="1-token decode against a 32768-key cache, 64-way split-KV + combine"),
+        Workload(
+            "chunk_prefill_b1h32kv8_nq2048_nk16384_d128", B=1, H=32, H_kv=8, Nq=2048, Nk=16384, d=128,
+            dtype="bf16", causal=True, causal_align="bottom_right", seed=6000,
+            description="a 2048-token prompt chunk appended to a 14336-token cache (bottom-right causal), "
+                        "four query heads per K/V head"),
+        Workload(
+            "decode_gqa_b16h32kv8_nk32768_d128", B=16, H=32, H_kv=8, Nq=1, Nk=32768, d=128, dtype="bf16",
+            causal=False, seed=7000, num_splits=64,
+            description="1-token decode with four query heads per K/V head, 64-way split-KV + combine"),
     ]
 }
 

@@ -72,6 +72,48 @@ def test_fwd_validation(L):
     assert fwd(L, scale=float("nan")) == 7
 
 
+def fwd_ex(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=4, H_kv=2, Nq=128, Nk=256, d=64, mask=1, scale=0.125, dtype=BF16):
+    vp = ctypes.c_void_p
+    return L.fa_fwd_ex(vp(q) if q else None, vp(k) if k else None, vp(v) if v else None, vp(o) if o else None,
+                       vp(lse) if lse else None, B, H, H_kv, Nq, Nk, d, mask, scale, dtype, None)
+
+
+def test_fwd_ex_validation(L):
+    assert fwd_ex(L, k=0) == 1
+    assert fwd_ex(L, d=80) == 4 and fwd_ex(L, dtype=5) == 4
+    assert fwd_ex(L, v=P_MIS) == 2
+    assert fwd_ex(L, H_kv=0) == 3 and fwd_ex(L, H_kv=3) == 3 and fwd_ex(L, H_kv=8) == 3  # must divide H
+    assert fwd_ex(L, mask=2, Nq=300, Nk=200) == 3  # bottom-right: the first rows would see no key
+    assert fwd_ex(L, mask=3) == 7 and fwd_ex(L, mask=-1) == 7
+    assert fwd_ex(L, scale=0.0) == 7
+    assert fwd_ex(L, B=2**20, H=2**20, H_kv=2**20) == 3
+    # shapes fa_fwd rejects but fa_fwd_ex accepts: validation passes, and with no GPU in this
+    # process the device query then fails (FA_ERR_HIP) before anything could be launched
+    no_gpu = 6
+    assert fwd(L, causal=1, Nq=128, Nk=256) == 3
+    assert fwd_ex(L, mask=1, Nq=128, Nk=256) in (0, no_gpu)
+    assert fwd_ex(L, mask=1, Nq=300, Nk=200) in (0, no_gpu)
+    assert fwd_ex(L, mask=2, Nq=200, Nk=300) in (0, no_gpu)
+    assert fwd_ex(L, H_kv=1, mask=0) in (0, no_gpu) and fwd_ex(L, H_kv=4, mask=0) in (0, no_gpu)
+
+
+def split_ex(L, q=P, k=P, v=P, ws=P, wsb=None, B=2, H=4, H_kv=2, Nk=100, d=128, scale=0.1, S=4, dtype=BF16):
+    vp = ctypes.c_void_p
+    if wsb is None:
+        wsb = fa.fa_decode_workspace_bytes(B, H, d, S) if S > 0 else 0
+    return L.fa_decode_split_ex(vp(q) if q else None, vp(k) if k else None, vp(v) if v else None,
+                                vp(ws) if ws else None, wsb, B, H, H_kv, Nk, d, scale, S, dtype, None)
+
+
+def test_decode_split_ex_validation(L):
+    assert split_ex(L, ws=0) == 1
+    assert split_ex(L, d=32) == 4
+    assert split_ex(L, k=P_MIS) == 2
+    assert split_ex(L, H_kv=0) == 3 and split_ex(L, H_kv=3) == 3 and split_ex(L, H_kv=8) == 3
+    assert split_ex(L, S=0, wsb=1 << 20) == 7 and split_ex(L, S=101) == 7
+    assert split_ex(L, wsb=fa.fa_decode_workspace_bytes(2, 4, 128, 4) - 1) == 5
+
+
 def test_decode_workspace_bytes(L):
     assert fa.fa_decode_workspace_bytes(16, 32, 128, 64) == 16 * 32 * 64 * 130 * 4
     assert fa.fa_decode_workspace_bytes(0, 32, 128, 64) == 0
