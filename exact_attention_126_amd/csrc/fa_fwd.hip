@@ -451,7 +451,10 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
 
 // Persistent kernel: one workgroup per CU loops over work items.  A causal item is the pair of
 // query blocks q and n_qblk - 1 - q of one head (heaviest first), so every item streams the
-// same number of tiles and the CUs stay balanced; a non-causal item is one query block.  With
+// same number of tiles and the CUs stay balanced; a non-causal item is one query block, and so
+// is a causal one when pairing would leave CUs idle (fewer pairs than CUs: the blocks then run
+// heaviest first, one per CU, which for a short query chunk against a long cache are nearly
+// equal anyway).  With
 // xcd_split, the items of XCD x (workgroups b with b % 8 == x) are a contiguous range ordered
 // by head, so the 32 CUs of an XCD work on about two heads at a time and share their K/V in
 // that XCD's L2.
@@ -459,7 +462,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int n_items, int items_per_head,
-    int xcd_split, float sl2, int H, int group, int diag) {
+    int xcd_split, float sl2, int H, int group, int diag, int paired) {
   using C = Bf16Cfg<D>;
   // Two-slot rings for K and V tiles.  Separate arrays let the compiler see that reads of one
   // slot never alias the asynchronous loads into another.
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int bh = it / items_per_head, r = it % items_per_head;
     const int kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
     const int qa = CAUSAL ? n_qblk - 1 - r : r;
-    const int cnt = (CAUSAL && r != qa) ? 2 : 1;
+    const int cnt = (CAUSAL && paired && r != qa) ? 2 : 1;
     for (int k = 0; k < cnt; ++k)
       fwd_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, k == 0 ? qa : r, n_qblk, kb0, kb1, vb0,
                            vb1);
@@ -609,14 +612,15 @@ template <int D, bool CAUSAL>
 hipError_t launch_bf16_impl(const FwdArgs& a, hipStream_t stream) {
   using C = Bf16Cfg<D>;
   const int n_qblk = (a.Nq + C::BR - 1) / C::BR;
-  const int items_per_head = CAUSAL ? (n_qblk + 1) / 2 : n_qblk;
+  const int paired = (CAUSAL && (int64_t)a.B * a.H * ((n_qblk + 1) / 2) >= a.num_cus) ? 1 : 0;
+  const int items_per_head = paired ? (n_qblk + 1) / 2 : n_qblk;
   const int64_t n_items = (int64_t)a.B * a.H * items_per_head;
   const int64_t grid = n_items < a.num_cus ? n_items : a.num_cus;
   const int xcd_split = (grid % 8 == 0 && n_items % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.Nq, a.Nk, n_qblk, (int)n_items, items_per_head, xcd_split, a.scale * kLog2e, a.H,
-                     a.H / a.H_kv, a.diag);
+                     a.H / a.H_kv, a.diag, paired);
   return hipGetLastError();
 }
 
