@@ -1,7 +1,7 @@
 """Benchmark of the exact fused attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-baseline on|off] [--copy-calibration]
-                    [--mfma-ceiling on|off]
+                    [--mfma-ceiling on|off] [--extras on|off]
 
 One step is one pass of the whole path over one batch of synthetic input:
   * the fused causal forward (fa_fwd) on B=8, H=16, Nq=Nk=8192, d=128, bf16, K scaled x2;
@@ -20,6 +20,10 @@ The printed JSON line carries:
   decode       decode KV-read GB/s (K and V read once) with its own HBM roofline
   cpu_baseline the float64 reference implementation timed on the host cores on a sample
                of the same workload (a reported baseline only)
+  extras       the extended entry points, timed separately after the steps (not part of
+               `value`): a bottom-right causal, grouped-K/V-head prefill chunk (fa_fwd_ex,
+               FLOPs counted over the visible query-key pairs) and a grouped-K/V-head decode
+               (fa_decode_split_ex + fa_decode_combine, GB/s of K/V bytes read once)
 HBM traffic measured with rocprofv3 counters is read from profiles/ when the summary there
 was taken on the current kernel sources, else reported as null.
 """
@@ -187,6 +191,54 @@ def sustained_mfma_ceiling(torch, warm_s: float = 0.3, reps: int = 20) -> dict |
             "operands": "bf16 N(0,1), seeded", "warm_s": warm_s}
 
 
+def time_extras(torch, fa, si, get, reps: int = 20) -> dict:
+    """The extended entry points on their own workloads, each timed over `reps` launches after a
+    warm-up, with HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = {}
+    w = get("chunk_prefill_b1h32kv8_nq2048_nk16384_d128")
+    dev = {x: to_device(w, si.make_tensor(w, x)) for x in "qkv"}
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: fa.fa_fwd_ex(dev["q"], dev["k"], dev["v"], o, lse, fa.FA_MASK_CAUSAL_BOTTOM_RIGHT, w.scale,
+                                    stream=stream), 2 * reps, 2 * reps)
+    pairs = sum(min(w.Nk, i + w.diag + 1) for i in range(w.Nq))  # visible (query, key) pairs per head
+    tf = 4.0 * w.B * w.H * pairs * w.d / (ms * 1e-3) / 1e12
+    out["chunked_prefill"] = {"workload": w.name, "entry": "fa_fwd_ex (bottom-right causal, H_kv=8)",
+                              "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4),
+                              "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    del dev, o, lse
+    w = get("decode_gqa_b16h32kv8_nk32768_d128")
+    dev = {x: to_device(w, si.make_tensor(w, x)) for x in "qkv"}
+    ws = fa.decode_workspace(dev["q"], w.num_splits)
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((w.B, w.H, 1), dtype=torch.float32, device="cuda")
+    ms_s = timed(lambda: fa.fa_decode_split_ex(dev["q"], dev["k"], dev["v"], ws, w.num_splits, w.scale,
+                                               stream=stream), reps, 3)
+    ms_c = timed(lambda: fa.fa_decode_combine(ws, o, lse, w.num_splits, stream=stream), reps, 3)
+    kv = 2.0 * w.B * w.kv_heads * w.Nk * w.d * w.elt_bytes
+    gbs = kv / ((ms_s + ms_c) * 1e-3) / 1e9
+    out["decode_gqa"] = {"workload": w.name, "entry": "fa_decode_split_ex + fa_decode_combine (H_kv=8)",
+                         "value": round(gbs, 1), "unit": "GB/s (K/V bytes read once)",
+                         "split_ms": round(ms_s, 4), "combine_ms": round(ms_c, 4),
+                         "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
+    del dev, ws, o, lse
+    return out
+
+
 def to_device(w, x):
     import numpy as np
     import torch
@@ -199,6 +251,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--extras", choices=["on", "off"], default="on",
+                    help="after the timed steps, time the extended entry points on their own workloads")
     ap.add_argument("--mfma-ceiling", choices=["on", "off"], default="on",
                     help="after the timed steps, measure the sustained bf16 MFMA rate (libfa_calib.so)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -285,6 +339,8 @@ def main():
     dec_gbs = kv_bytes / ((ms_split + ms_comb) * 1e-3) / 1e9
     split_gbs = kv_bytes / (ms_split * 1e-3) / 1e9
 
+    del dp, dd, o, lse, od, lsed, ws
+    extras = time_extras(torch, fa, si, get) if args.extras == "on" else None
     ceiling = sustained_mfma_ceiling(torch) if args.mfma_ceiling == "on" else None
     tr_f = read_traffic("fwd_bf16_prefill_b8h16_n8192_d128_causal_hbm_traffic.txt", FWD_SOURCES)
     tr_d = read_traffic("decode_split_b16h32_nk32768_d128_hbm_traffic.txt", DEC_SOURCES)
@@ -317,6 +373,7 @@ def main():
                                 "traffic": None if tr_d is None else tr_d["bytes"]},
                    "cpu_baseline": cpu_dec},
         "cpu_baseline": cpu_pre,
+        "extras": extras,
     }
     print(json.dumps(line), flush=True)
 
