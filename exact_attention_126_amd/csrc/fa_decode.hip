@@ -7,11 +7,14 @@
 // "FlashAttention 为什么快", follow-up 3).  The merge rescales every partial result by
 // exp(m_s - max m) before summing (same answer, follow-up 2).
 //
-// decode_split_kernel: one workgroup per (batch*head, split).  D/8 (bf16) or D/4 (fp32) lanes
-// share a key row and read it with coalesced 16-byte loads; each wave walks its own keys with
-// an online softmax (running max, running sum, rescaled accumulator, Day-21 page §5.2-5.3),
-// U key rows of K and of V in flight per lane.  The four waves' states are merged through
-// LDS and written to the workspace as (O_part, m, l).
+// decode_split_kernel: one workgroup per (batch, group of query heads sharing a K/V head, split).
+// D/8 (bf16) or D/4 (fp32) lanes share a key row and read it with coalesced 16-byte loads; each
+// wave walks its own keys with an online softmax per query head (running max, running sum,
+// rescaled accumulator, Day-21 page §5.2-5.3), U key rows of K and of V in flight per lane.
+// With grouped K/V heads (several query heads per K/V head, which the Day-21 page's FAQ Q5
+// names among the decode-side techniques) a workgroup serves up to four query heads from one
+// read of the K/V rows.  The four waves' states are merged through LDS and written to the
+// workspace as (O_part, m, l) per query head.
 // decode_combine_kernel: one workgroup per (batch*head), one thread per dim.
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -63,7 +66,11 @@ struct Elt<float> {
   __device__ static float narrow(float x) { return x; }
 };
 
-template <typename T, int D>
+// One workgroup per (batch, group of GE query heads that share a K/V head, split): the K/V rows
+// of the split are read once and serve all GE heads.  Each head's arithmetic is the same
+// whatever GE is (per-head dot products, maxima, sums and accumulators in the same order), so a
+// grouped call gives bit for bit what an ungrouped call on repeated K/V heads gives.
+template <typename T, int D, int GE>
 __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, float* __restrict__ Opart,
                                                            float* __restrict__ ML, int Nk, int S, int chunk,
@@ -71,27 +78,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
   constexpr int EPL = Elt<T>::PER16;  // elements per lane per key row
   constexpr int LPK = D / EPL;        // lanes per key row
   constexpr int KPW = 64 / LPK;       // key rows per wave per step
-  constexpr int U = 8;                // steps in flight per iteration
+  constexpr int U = 8;                // steps in flight per iteration (the same for every GE)
   constexpr int WAVES = 4;
-  __shared__ float s_m[WAVES], s_l[WAVES];
-  __shared__ float s_acc[WAVES][D];
+  __shared__ float s_m[WAVES][GE], s_l[WAVES][GE];
+  __shared__ float s_acc[WAVES][GE][D];
 
   const int s = blockIdx.x % S;
-  const int bh = blockIdx.x / S;
+  const int bh0 = (blockIdx.x / S) * GE;  // first query head (b * H + h) of this workgroup's group
   const int start = s * chunk;
   const int end = min(Nk, start + chunk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int gi = lane / LPK, li = lane % LPK;
 
-  float qv[EPL];
-  Elt<T>::widen(gload16(Q + (int64_t)bh * D + li * EPL), qv);
-  const int kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
+  float qv[GE][EPL];
+#pragma unroll
+  for (int g = 0; g < GE; ++g) Elt<T>::widen(gload16(Q + (int64_t)(bh0 + g) * D + li * EPL), qv[g]);
+  const int kvh = (bh0 / H) * (H / group) + (bh0 % H) / group;  // K/V head shared by the GE query heads
   const T* Kh = K + (int64_t)kvh * Nk * D + li * EPL;
   const T* Vh = V + (int64_t)kvh * Nk * D + li * EPL;
 
-  float m = -INFINITY, l = 0.f, acc[EPL];
+  float m[GE], l[GE], acc[GE][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int g = 0; g < GE; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
 
   for (int base = start + wave * U * KPW; base < end; base += WAVES * U * KPW) {
     u32x4_t kr[U], vr[U];
@@ -101,69 +114,85 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
       kr[u] = gload16(Kh + (int64_t)key * D);
       vr[u] = gload16(Vh + (int64_t)key * D);
     }
-    float sc[U];
-    float bm = -INFINITY;
+    float sc[U][GE];
+    float bm[GE];
+#pragma unroll
+    for (int g = 0; g < GE; ++g) bm[g] = -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kf[EPL];
       Elt<T>::widen(kr[u], kf);
-      float dot = 0.f;
+      const bool in = base + u * KPW + gi < end;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
-      dot = group_sum<LPK>(dot);
-      sc[u] = (base + u * KPW + gi < end) ? dot * sl2 : -INFINITY;
-      bm = fmaxf(bm, sc[u]);
+      for (int g = 0; g < GE; ++g) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[g][e], kf[e], dot);
+        dot = group_sum<LPK>(dot);
+        sc[u][g] = in ? dot * sl2 : -INFINITY;
+        bm[g] = fmaxf(bm[g], sc[u][g]);
+      }
     }
 #pragma unroll
-    for (int w = LPK; w < 64; w <<= 1) bm = fmaxf(bm, __shfl_xor(bm, w));
-    const float mnew = fmaxf(m, bm);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    l *= alpha;
+    for (int g = 0; g < GE; ++g) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+      for (int w = LPK; w < 64; w <<= 1) bm[g] = fmaxf(bm[g], __shfl_xor(bm[g], w));
+      const float mnew = fmaxf(m[g], bm[g]);
+      const float alpha = fast_exp2(m[g] - mnew);
+      m[g] = mnew;
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float p = fast_exp2(sc[u] - mnew);
       float vf[EPL];
       Elt<T>::widen(vr[u], vf);
-      l += p;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(p, vf[e], acc[e]);
+      for (int g = 0; g < GE; ++g) {
+        const float p = fast_exp2(sc[u][g] - m[g]);
+        l[g] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = __builtin_fmaf(p, vf[e], acc[g][e]);
+      }
     }
   }
   // fold the key groups of the wave: lanes with equal li hold the same dims
 #pragma unroll
-  for (int w = LPK; w < 64; w <<= 1) {
-    l += __shfl_xor(l, w);
+  for (int g = 0; g < GE; ++g) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], w);
-  }
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_l[wave] = l;
-  }
-  if (gi == 0) {
+    for (int w = LPK; w < 64; w <<= 1) {
+      l[g] += __shfl_xor(l[g], w);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s_acc[wave][li * EPL + e] = acc[e];
+      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], w);
+    }
+    if (lane == 0) {
+      s_m[wave][g] = m[g];
+      s_l[wave][g] = l[g];
+    }
+    if (gi == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][g][li * EPL + e] = acc[g][e];
+    }
   }
   __syncthreads();
-  if (tid < D) {
-    float M = s_m[0];
+  for (int x = tid; x < GE * D; x += 256) {
+    const int g = x / D, dim = x % D;
+    float M = s_m[0][g];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, s_m[w]);
+    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, s_m[w][g]);
     float o = 0.f, L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        const float f = fast_exp2(s_m[w] - M);
-        o = __builtin_fmaf(f, s_acc[w][tid], o);
-        L = __builtin_fmaf(f, s_l[w], L);
+        const float f = fast_exp2(s_m[w][g] - M);
+        o = __builtin_fmaf(f, s_acc[w][g][dim], o);
+        L = __builtin_fmaf(f, s_l[w][g], L);
       }
     }
-    const int64_t rec = (int64_t)bh * S + s;
-    Opart[rec * D + tid] = o;
-    if (tid == 0) {
+    const int64_t rec = (int64_t)(bh0 + g) * S + s;
+    Opart[rec * D + dim] = o;
+    if (dim == 0) {
       ML[rec * 2] = (M == -INFINITY) ? -INFINITY : M * kLn2;
       ML[rec * 2 + 1] = L;
     }
@@ -190,19 +219,33 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
   if (dim == 0) LSE[bh] = M + fast_log2(L) * kLn2;
 }
 
+template <typename T, int D, int GE>
+void launch_split(const DecodeSplitArgs& a, int chunk, float sl2, hipStream_t stream) {
+  const int64_t nblk = (int64_t)a.B * (a.H / GE) * a.num_splits;
+  hipLaunchKernelGGL((decode_split_kernel<T, D, GE>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2, a.H,
+                     a.H / a.H_kv);
+}
+
+template <typename T, int D>
+void launch_split_d(const DecodeSplitArgs& a, int chunk, float sl2, hipStream_t stream) {
+  const int group = a.H / a.H_kv;  // query heads per K/V head; a workgroup takes 4, 2 or 1 of them
+  if (group % 4 == 0)
+    launch_split<T, D, 4>(a, chunk, sl2, stream);
+  else if (group % 2 == 0)
+    launch_split<T, D, 2>(a, chunk, sl2, stream);
+  else
+    launch_split<T, D, 1>(a, chunk, sl2, stream);
+}
+
 template <typename T>
 hipError_t split_impl(const DecodeSplitArgs& a, hipStream_t stream) {
   const int chunk = (a.Nk + a.num_splits - 1) / a.num_splits;
-  const int64_t nblk = (int64_t)a.B * a.H * a.num_splits;
   const float sl2 = a.scale * kLog2e;
   if (a.d == 128)
-    hipLaunchKernelGGL((decode_split_kernel<T, 128>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T*)a.q,
-                       (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2, a.H,
-                       a.H / a.H_kv);
+    launch_split_d<T, 128>(a, chunk, sl2, stream);
   else
-    hipLaunchKernelGGL((decode_split_kernel<T, 64>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T*)a.q,
-                       (const T*)a.k, (const T*)a.v, a.o_part, a.ml, a.Nk, a.num_splits, chunk, sl2, a.H,
-                       a.H / a.H_kv);
+    launch_split_d<T, 64>(a, chunk, sl2, stream);
   return hipGetLastError();
 }
 
