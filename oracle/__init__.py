@@ -14,6 +14,7 @@ Modules:
                 the per-split partials and their merge for split-KV decode.
   recurrence  - the online-softmax block recurrence in pure Python (tiny inputs only),
                 used to pin the block-by-block steps against the two-pass definition.
+  backward    - the gradients dQ, dK, dV by the chain rule through the same definition.
 
 Every function here is pinned by tests marked "not gpu" (closed forms, invariants,
 library special cases, brute force and the pages' own worked example).
@@ -22,4 +23,5 @@ from .attention import (  # noqa: F401
     scores, softmax_two_pass, attention_head, attention, attention_probs,
     split_bounds, split_partials, combine_partials,
 )
+from .backward import attention_backward_head, attention_backward, softmax_row_stat  # noqa: F401
 from . import recurrence  # noqa: F401
