@@ -43,7 +43,8 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLO
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PREFILL = "prefill_b8h16_n8192_d128_causal"
 DECODE = "decode_b16h32_nk32768_d128"
-FWD_SOURCES = ["exact_attention_126_amd/csrc/fa_fwd.hip", "exact_attention_126_amd/csrc/fa_device.h"]
+FWD_SOURCES = ["exact_attention_126_amd/csrc/fa_fwd.hip", "exact_attention_126_amd/csrc/fa_device.h",
+               "exact_attention_126_amd/csrc/fa_tile_layout.h"]
 DEC_SOURCES = ["exact_attention_126_amd/csrc/fa_decode.hip", "exact_attention_126_amd/csrc/fa_device.h"]
 
 

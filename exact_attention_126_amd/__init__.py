@@ -27,7 +27,7 @@ FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE", 4: "FA_ERR_UNSUPPORTED",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
 EXPORTED = ["fa_fwd", "fa_fwd_ex", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_split_ex",
-            "fa_decode_combine", "fa_status_string"]
+            "fa_decode_combine", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string"]
 
 _lib = None
 
@@ -58,6 +58,11 @@ def lib() -> ctypes.CDLL:
         L.fa_decode_split.restype = i32
         L.fa_decode_combine.argtypes = [vp, ctypes.c_size_t, vp, vp, i64, i64, i64, i32, i32, vp]
         L.fa_decode_combine.restype = i32
+        L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, i64, i32,
+                             f32, i32, vp]
+        L.fa_bwd.restype = i32
         L.fa_status_string.argtypes = [i32]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -194,6 +199,33 @@ def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None) -> None:
     _raise(st, "fa_decode_combine")
 
 
+def fa_bwd_workspace_bytes(B: int, H: int, Nq: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, H, Nq))
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, mask=FA_MASK_NONE, scale: float | None = None,
+           stream=None) -> None:
+    """Gradients dq [B,H,Nq,d], dk and dv [B,H_kv,Nk,d] (bf16) of a loss with gradient do w.r.t. the
+    forward's o, recomputing P from q, k and the forward's lse; workspace of fa_bwd_workspace_bytes."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, q.dtype)
+    _check(lse, "lse", torch.float32)
+    _check(workspace, "workspace")
+    _check_shapes(q, k, v, o, lse, same_heads=False)
+    if tuple(do.shape) != tuple(q.shape) or tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) \
+            or tuple(dv.shape) != tuple(k.shape):
+        raise ValueError("do and dq must have the shape of q, dk and dv the shape of k")
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    m = MASKS[mask] if isinstance(mask, str) else int(mask)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, H_kv, Nq, Nk, d, m,
+                      float(scale), _dtype_code(q), _stream(stream))
+    _raise(st, "fa_bwd")
+
+
 # ---- conveniences that allocate the outputs with torch and call the entry points above
 def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=None, mask=None):
     """(o, lse) = attention(q, k, v): allocates the outputs and calls fa_fwd, or fa_fwd_ex when
@@ -228,3 +260,14 @@ def decode(q, k, v, num_splits: int, scale: float | None = None, workspace=None,
         fa_decode_split_ex(q, k, v, workspace, num_splits, scale, stream)
     fa_decode_combine(workspace, o, lse, num_splits, stream)
     return o, lse
+
+
+def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None, mask=None):
+    """(dq, dk, dv) for the forward (o, lse) = attention(q, k, v, causal / mask, scale): allocates the
+    gradients and the workspace and calls fa_bwd."""
+    B, H, Nq, _ = q.shape
+    ws = torch.empty(fa_bwd_workspace_bytes(B, H, Nq) // 4, dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, (FA_MASK_CAUSAL if causal else FA_MASK_NONE) if mask is None else mask,
+           scale, stream)
+    return dq, dk, dv

@@ -118,6 +118,35 @@ fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, voi
                                          : fa::launch_decode_combine_f32(a, stream));
 }
 
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || B > kI32Max / H || B * H > kI32Max / Nq) return 0;
+  return (size_t)(B * H * Nq) * 2 * sizeof(float);
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                   int64_t H_kv, int64_t Nq, int64_t Nk, int64_t d, fa_mask_t mask, float scale, fa_dtype_t dtype,
+                   hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  if (dtype != FA_DTYPE_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_CAUSAL_BOTTOM_RIGHT) return FA_ERR_ARG;
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Nq <= 0 || Nk <= 0 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (mask == FA_MASK_CAUSAL_BOTTOM_RIGHT && Nk < Nq) return FA_ERR_SHAPE;
+  if (!head_fits(Nq, d, dtype) || !head_fits(Nk, d, dtype)) return FA_ERR_SHAPE;
+  // the workspace (2 floats per query row) is addressed with 32-bit byte offsets
+  if (B > kI32Max / H || B * H > kI32Max / 8 / Nq) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_ARG;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq)) return FA_ERR_WORKSPACE;
+  const bool causal = mask != FA_MASK_NONE;
+  const int diag = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT ? (int)(Nk - Nq) : 0;
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace), (int)B, (int)H, (int)Nq, (int)Nk,
+                (int)d, (int)H_kv, causal, diag, scale};
+  return from_hip(fa::launch_bwd_bf16(a, stream));
+}
+
 const char* fa_status_string(fa_status_t s) {
   switch (s) {
     case FA_OK: return "ok";
@@ -127,7 +156,7 @@ const char* fa_status_string(fa_status_t s) {
       return "invalid shape (size <= 0, H_kv not dividing H, a causal alignment some row sees no key under, "
              "or beyond index limits)";
     case FA_ERR_UNSUPPORTED: return "unsupported head dim (64 or 128) or dtype";
-    case FA_ERR_WORKSPACE: return "decode workspace too small";
+    case FA_ERR_WORKSPACE: return "workspace smaller than the size its *_workspace_bytes function returns";
     case FA_ERR_HIP: return "HIP runtime error at launch";
     case FA_ERR_ARG:
       return "invalid scalar argument (scale must be finite and > 0; 1 <= num_splits <= Nk; known mask)";

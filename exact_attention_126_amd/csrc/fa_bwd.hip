@@ -1,0 +1,454 @@
+// Backward pass of exact attention for gfx950: dQ, dK, dV from Q, K, V, O, dO and the forward's
+// per-row LSE, recomputing the probabilities tile by tile instead of storing them (M4-047 card
+// "高效注意力与 FlashAttention", §3 point (c); the Day-21 page "GPU 学习日报 Day 21：
+// FlashAttention：GPU Memory Hierarchy 下的 IO 优化", §3.2, notes that a standard implementation
+// keeps the N x N probabilities for the backward instead).  For one head:
+//     P = exp(scale Q K^T - LSE)  (0 where masked),   dV = P^T dO,   dP = dO V^T,
+//     dS = P * (dP - Dr),  Dr_i = dO_i . O_i,         dQ = scale dS K,  dK = scale dS^T Q
+// (the chain rule through softmax; Dr_i equals rowsum(P * dP) because O = P V).
+//
+// Three kernels, all on one stream, with no atomics (the result is bit-reproducible):
+//  * bwd_pre_kernel: Dr and LSE in log2 units per query row, into the caller's workspace.
+//  * bwd_dq_kernel: query-major like the forward.  Each wave owns 32 queries and streams 32-key
+//    K/V tiles through LDS (LDS DMA, double buffered): S^T = K Q^T and dP^T = V dO^T on
+//    v_mfma_f32_32x32x16_bf16 with Q^T and dO^T held in VGPRs, then dS^T in VGPRs, then
+//    dQ^T += K^T dS^T with K^T read from LDS by the transposing ds_read_b64_tr_b16.  The
+//    accumulator-to-B-operand key order (key_of_row) is the forward's.
+//  * bwd_dkdv_kernel: key-major.  Each wave owns 16 keys, with their K and V fragments in VGPRs,
+//    and streams 32-query tiles of Q, dO, LSE and Dr through LDS: S = Q K^T and dP = dO V^T on
+//    v_mfma_f32_16x16x32_bf16, then P and dS, then dV^T += dO^T P and dK^T += Q^T dS.  Query
+//    rows are loaded in the order that makes the 16x16 accumulators directly the B operands of
+//    the last two products.  With grouped K/V heads the workgroup loops over the query heads that
+//    share its K/V head and its dK, dV sum over them.
+// Recomputing S and dP in both big kernels costs 7 matrix products instead of 5, and keeps both
+// free of the cross-workgroup dQ reduction a single kernel would need.
+#include "fa_device.h"
+#include "fa_launch.h"
+#include "fa_tile_layout.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// ------------------------------------------------------------------ preprocess
+// One 16-lane group per query row: Dr = dO . O (fp32 sum of bf16 products), L2 = LSE * log2 e.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                                                      const float* __restrict__ LSE, float* __restrict__ L2,
+                                                      float* __restrict__ Dr, int64_t rows) {
+  constexpr int LPR = 16, EPL = D / LPR;  // lanes per row, elements per lane (8 or 4)
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int li = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint16_t* op = O + row * D + li * EPL;
+    const uint16_t* dp = dO + row * D + li * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = __builtin_fmaf(bf16_bits_to_f32(op[e]), bf16_bits_to_f32(dp[e]), acc);
+  }
+#pragma unroll
+  for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
+  if (row < rows && li == 0) {
+    Dr[row] = acc;
+    L2[row] = LSE[row] * kLog2e;
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D>
+struct DqCfg {
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int BR = WAVES * 32;  // queries per workgroup
+  static constexpr int BC = 32;          // keys per tile
+  static constexpr int RB = D * 2;       // bytes per LDS row
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BC * RB;
+  static constexpr int ROWS_PER_DMA = 64 / CPR;
+  static constexpr int DMAS = TILE_BYTES / 1024;                  // per tensor and tile
+  static constexpr int DMA_PER_WAVE = (2 * DMAS + WAVES - 1) / WAVES;  // K and V together
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DBLK = D / 32;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dr,
+    uint16_t* __restrict__ dQ, int H, int group, int Nq, int Nk, int n_qblk, float scale, float sl2, int diag) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char kb[2][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb[2][C::TILE_BYTES];
+
+  // heaviest query blocks first (causal), each head's blocks together
+  const int qblk = CAUSAL ? n_qblk - 1 - (int)(blockIdx.x % n_qblk) : (int)(blockIdx.x % n_qblk);
+  const int bh = blockIdx.x / n_qblk;
+  const int kvh = (bh / H) * (H / group) + (bh % H) / group;
+  const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
+  const uint16_t* Vh = V + (int64_t)kvh * Nk * D;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q_wave0 = qblk * C::BR + wave * 32;
+  const int q = q_wave0 + l32;
+  const int qc = min(q, Nq - 1);
+
+  // Q^T and dO^T fragments (B operands), resident for the whole block
+  bf16x8_t qf[C::KSTEPS], dof[C::KSTEPS];
+  {
+    const uint16_t* qp = Q + ((int64_t)bh * Nq + qc) * D + 8 * hh;
+    const uint16_t* dp = dO + ((int64_t)bh * Nq + qc) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      qf[ks] = as_bf16x8(gload16(qp + 16 * ks));
+      dof[ks] = as_bf16x8(gload16(dp + 16 * ks));
+    }
+  }
+  const float l2 = L2[(int64_t)bh * Nq + qc];
+  const float dr = Dr[(int64_t)bh * Nq + qc];
+
+  const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR + diag) : Nk;
+  const int n = (kv_end + C::BC - 1) / C::BC;
+
+  // tile loads: instruction x of a tile moves 1 KiB of K (x < DMAS) or V; lane L lands in row
+  // L / CPR, slot L % CPR of the instruction's rows and fetches the chunk the swizzle puts there
+  const __amdgpu_buffer_rsrc_t Kr = raw_rsrc(Kh, Nk * C::RB), Vr = raw_rsrc(Vh, Nk * C::RB);
+  auto issue = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const int x = wave + C::WAVES * i;
+      if (x < 2 * C::DMAS) {
+        const int c = x < C::DMAS ? x : x - C::DMAS;
+        const int row = c * C::ROWS_PER_DMA + lane / C::CPR;
+        const uint32_t off =
+            (uint32_t)min(t * C::BC + row, Nk - 1) * C::RB + (((lane % C::CPR) ^ swz<D>(row)) << 4);
+        if (x < C::DMAS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(Kr, (lptr_t)(kb[buf] + c * 1024), 16, off, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(Vr, (lptr_t)(vb[buf] + c * 1024), 16, off, 0, 0, 0);
+      }
+    }
+  };
+
+  // per-lane LDS offsets: 16-byte row reads of permuted keys (A of S^T and dP^T) and transposing
+  // 8-byte reads of K^T (A of dQ^T)
+  int koff[C::KSTEPS];
+  {
+    const int krow = key_of_row(l32);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) koff[ks] = krow * C::RB + (((2 * ks + hh) ^ swz<D>(krow)) << 4);
+  }
+  int toff[C::DBLK][2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const int vh = g >> 1, ve = s >> 2, vq = s & 3;
+#pragma unroll
+    for (int mb = 0; mb < C::DBLK; ++mb)
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        const int key = 8 * vh + 4 * I + ve;
+        const int dim = 32 * mb + 16 * (g & 1) + 4 * vq;
+        toff[mb][I] = key * C::RB + (((dim >> 3) ^ swz<D>(key)) << 4) + ((dim >> 2) & 1) * 8;
+      }
+  }
+
+  f32x16_t dq[C::DBLK];
+#pragma unroll
+  for (int mb = 0; mb < C::DBLK; ++mb) dq[mb] = f32x16_t{};
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  for (int t = 0; t < n; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < n) issue(t + 1, cur ^ 1);
+    const FA_LDS char* kt = (const FA_LDS char*)kb[cur];
+    const FA_LDS char* vt = (const FA_LDS char*)vb[cur];
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_load16(kt + koff[ks])), qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_load16(vt + koff[ks])), dof[ks], dp, 0, 0, 0);
+    }
+    // P^T and dS^T; register j of lane-half hh holds key 16 (j / 8) + 8 hh + j % 8 of the tile
+    const int tile0 = t * C::BC;
+    const bool need_mask = (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag);
+    const int lim = CAUSAL ? min(Nk - 1, q + diag) : Nk - 1;
+    u32x4_t dsb[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = 8 * t2 + 2 * u + e;
+          float p = fast_exp2(__builtin_fmaf(s[j], sl2, -l2));
+          if (need_mask && tile0 + 16 * t2 + 8 * hh + 2 * u + e > lim) p = 0.f;
+          v2[e] = p * (dp[j] - dr);
+        }
+        dsb[t2][u] = pack_bf16x2(v2[0], v2[1]);
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int mb = 0; mb < C::DBLK; ++mb) {
+        const i16x4_t lo = lds_load8_tr16(kt + toff[mb][0] + t2 * 16 * C::RB);
+        const i16x4_t hi = lds_load8_tr16(kt + toff[mb][1] + t2 * 16 * C::RB);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dq[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(dsb[t2]), dq[mb], 0, 0, 0);
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
+    __syncthreads();                     // ... for every wave, and this tile's reads are done
+  }
+
+  if (q < Nq) {
+    uint16_t* op = dQ + ((int64_t)bh * Nq + q) * D + 4 * hh;
+#pragma unroll
+    for (int mb = 0; mb < C::DBLK; ++mb)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        u32x2_t w;
+        w[0] = pack_bf16x2(dq[mb][4 * jg + 0] * scale, dq[mb][4 * jg + 1] * scale);
+        w[1] = pack_bf16x2(dq[mb][4 * jg + 2] * scale, dq[mb][4 * jg + 3] * scale);
+        *(u32x2_t*)(op + 32 * mb + 8 * jg) = w;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int D>
+struct DkvCfg {
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int BK = WAVES * 16;  // keys per workgroup
+  static constexpr int BQ = 32;          // queries per tile
+  static constexpr int RB = D * 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE_BYTES = BQ * RB;
+  static constexpr int ROWS_PER_DMA = 64 / CPR;
+  static constexpr int DMAS = TILE_BYTES / 1024;                       // per tensor and tile
+  static constexpr int DMA_PER_WAVE = (2 * DMAS + WAVES - 1) / WAVES;  // Q and dO together
+  static constexpr int KS = D / 32;                                    // k-steps of S = Q K^T
+  static constexpr int DB = D / 16;                                    // 16-dim blocks of dK^T, dV^T
+};
+
+// Chunk swizzle of the 32-row Q and dO tiles: the 16 rows a 16-lane group reads at one chunk
+// (and the 4 rows x 4 pieces of a transposing read) spread over the banks.
+__device__ __forceinline__ int qswz(int row) { return row & 7; }
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ ws, int64_t rows_total,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H, int group, int Nq, int Nk, int n_kblk,
+    float scale, float sl2, int diag) {
+  using C = DkvCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char qb[2][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ob[2][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) float sb[2][2 * C::BQ];  // [L2 x 32][Dr x 32]
+
+  const int kblk = blockIdx.x % n_kblk;
+  const int bkv = blockIdx.x / n_kblk;  // b * H_kv + kv head
+  const int H_kv = H / group;
+  const int b = bkv / H_kv, hk = bkv % H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, L = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k0 = kblk * C::BK;
+  const int key = k0 + wave * 16 + L;  // this lane's key (column of every accumulator)
+  const int keyc = min(key, Nk - 1);
+
+  // K^T and V^T fragments (B operands of S and dP): key `key`, dims 32 ks + 8 G .. + 7
+  bf16x8_t kf[C::KS], vf[C::KS];
+  {
+    const uint16_t* kp = K + ((int64_t)bkv * Nk + keyc) * D + 8 * G;
+    const uint16_t* vp = V + ((int64_t)bkv * Nk + keyc) * D + 8 * G;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      kf[ks] = as_bf16x8(gload16(kp + 32 * ks));
+      vf[ks] = as_bf16x8(gload16(vp + 32 * ks));
+    }
+  }
+
+  // LDS offsets.  S and dP: A row r = L of 16-row block bl reads query 8 (r / 4) + 4 bl + r % 4
+  // of the tile, so accumulator register j of block bl in lane group G is query 8 G + 4 bl + j and
+  // the 8 values a lane holds are the B operand (k = queries 8 G .. 8 G + 7) of dV^T and dK^T.
+  int roff[2][C::KS];
+#pragma unroll
+  for (int bl = 0; bl < 2; ++bl) {
+    const int row = 8 * (L >> 2) + 4 * bl + (L & 3);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) roff[bl][ks] = row * C::RB + (((4 * ks + G) ^ qswz(row)) << 4);
+  }
+  // transposing reads for dO^T and Q^T (A of dV^T, dK^T): lane L of group G addresses query
+  // 8 G + 4 I + L / 4, dims 16 db + 4 (L % 4) .. + 3 (byte 32 db + 8 (L % 4) of the row); lane l
+  // receives dim 16 db + L of queries 8 G + 4 I .. + 3
+  auto tr_off = [&](int I, int db) {
+    const int row = 8 * G + 4 * I + (L >> 2);
+    return row * C::RB + (((2 * db + ((L & 3) >> 1)) ^ qswz(row)) << 4) + ((L & 1) ? 8 : 0);
+  };
+
+  f32x4v_t dk[C::DB], dv[C::DB];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) {
+    dk[i] = f32x4v_t{};
+    dv[i] = f32x4v_t{};
+  }
+
+  // query tiles this workgroup's keys can be seen from: query i sees key j iff j <= i + diag
+  const int q_first = CAUSAL ? max(0, k0 - diag) / C::BQ : 0;
+  const int n_qt = (Nq + C::BQ - 1) / C::BQ;
+  const __amdgpu_buffer_rsrc_t wsr = raw_rsrc(ws, (int)(2 * rows_total * 4));
+
+  for (int gh = 0; gh < group; ++gh) {
+    const int bh = b * H + hk * group + gh;  // query head
+    const uint16_t* Qh = Q + (int64_t)bh * Nq * D;
+    const uint16_t* Oh = dO + (int64_t)bh * Nq * D;
+    const __amdgpu_buffer_rsrc_t Qr = raw_rsrc(Qh, Nq * C::RB), Or = raw_rsrc(Oh, Nq * C::RB);
+    auto issue = [&](int t, int buf) {
+#pragma unroll
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+        const int x = wave + C::WAVES * i;
+        if (x < 2 * C::DMAS) {
+          const int c = x < C::DMAS ? x : x - C::DMAS;
+          const int row = c * C::ROWS_PER_DMA + lane / C::CPR;
+          const uint32_t off =
+              (uint32_t)min(t * C::BQ + row, Nq - 1) * C::RB + (((lane % C::CPR) ^ qswz(row)) << 4);
+          if (x < C::DMAS)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(Qr, (lptr_t)(qb[buf] + c * 1024), 16, off, 0, 0, 0);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(Or, (lptr_t)(ob[buf] + c * 1024), 16, off, 0, 0, 0);
+        }
+      }
+      if (wave == C::WAVES - 1) {  // L2 (lanes 0-31) and Dr (lanes 32-63) of the tile's queries
+        const int qq = min(t * C::BQ + (lane & 31), Nq - 1);
+        const uint32_t off = (uint32_t)(((lane >> 5) * rows_total + (int64_t)bh * Nq + qq) * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (lptr_t)(&sb[buf][0]), 4, off, 0, 0, 0);
+      }
+    };
+
+    if (q_first < n_qt) issue(q_first, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int t = q_first; t < n_qt; ++t) {
+      const int cur = (t - q_first) & 1;
+      if (t + 1 < n_qt) issue(t + 1, cur ^ 1);
+      const FA_LDS char* qt = (const FA_LDS char*)qb[cur];
+      const FA_LDS char* ot = (const FA_LDS char*)ob[cur];
+      const FA_LDS float* st = (const FA_LDS float*)sb[cur];
+      f32x4v_t s[2], dp[2];
+#pragma unroll
+      for (int bl = 0; bl < 2; ++bl) {
+        s[bl] = f32x4v_t{};
+        dp[bl] = f32x4v_t{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          s[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lds_load16(qt + roff[bl][ks])), kf[ks], s[bl], 0,
+                                                           0, 0);
+          dp[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lds_load16(ot + roff[bl][ks])), vf[ks], dp[bl],
+                                                            0, 0, 0);
+        }
+      }
+      // P and dS for queries q0 + 8 G + 4 bl + j against this lane's key
+      const int q0 = t * C::BQ;
+      const f32x4v_t l2a = *(const FA_LDS f32x4v_t*)(st + 8 * G);
+      const f32x4v_t l2b = *(const FA_LDS f32x4v_t*)(st + 8 * G + 4);
+      const f32x4v_t dra = *(const FA_LDS f32x4v_t*)(st + C::BQ + 8 * G);
+      const f32x4v_t drb = *(const FA_LDS f32x4v_t*)(st + C::BQ + 8 * G + 4);
+      u32x4_t pB, dsB;
+#pragma unroll
+      for (int bl = 0; bl < 2; ++bl)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          float pv[2], dsv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int j = 2 * j2 + e;
+            const int qq = q0 + 8 * G + 4 * bl + j;
+            const float l2 = bl ? l2b[j] : l2a[j];
+            const float dr = bl ? drb[j] : dra[j];
+            float p = fast_exp2(__builtin_fmaf(s[bl][j], sl2, -l2));
+            if (qq >= Nq || (CAUSAL && key > qq + diag)) p = 0.f;
+            pv[e] = p;
+            dsv[e] = p * (dp[bl][j] - dr);
+          }
+          pB[2 * bl + j2] = pack_bf16x2(pv[0], pv[1]);
+          dsB[2 * bl + j2] = pack_bf16x2(dsv[0], dsv[1]);
+        }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (k = the tile's 32 queries)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const i16x4_t olo = lds_load8_tr16(ot + tr_off(0, db));
+        const i16x4_t ohi = lds_load8_tr16(ot + tr_off(1, db));
+        const bf16x8_t ao = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, as_bf16x8(pB), dv[db], 0, 0, 0);
+        const i16x4_t qlo = lds_load8_tr16(qt + tr_off(0, db));
+        const i16x4_t qhi = lds_load8_tr16(qt + tr_off(1, db));
+        const bf16x8_t aq = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, as_bf16x8(dsB), dk[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
+  }
+
+  // dK = scale dK^T^T, dV = dV^T^T: register j of block db is dim 16 db + 4 G + j of key `key`
+  if (key < Nk) {
+    uint16_t* kp = dK + ((int64_t)bkv * Nk + key) * D + 4 * G;
+    uint16_t* vp = dV + ((int64_t)bkv * Nk + key) * D + 4 * G;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      u32x2_t wk, wv;
+      wk[0] = pack_bf16x2(dk[db][0] * scale, dk[db][1] * scale);
+      wk[1] = pack_bf16x2(dk[db][2] * scale, dk[db][3] * scale);
+      wv[0] = pack_bf16x2(dv[db][0], dv[db][1]);
+      wv[1] = pack_bf16x2(dv[db][2], dv[db][3]);
+      *(u32x2_t*)(kp + 16 * db) = wk;
+      *(u32x2_t*)(vp + 16 * db) = wv;
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_impl(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.H * a.Nq;
+  float* L2 = a.ws;
+  float* Dr = a.ws + rows;
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
+                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, L2, Dr, rows);
+  const float sl2 = a.scale * kLog2e;
+  const int group = a.H / a.H_kv;
+  {
+    using C = DqCfg<D>;
+    const int n_qblk = (a.Nq + C::BR - 1) / C::BR;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)a.B * a.H * n_qblk)), dim3(C::THREADS),
+                       0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, L2, Dr, (uint16_t*)a.dq, a.H, group, a.Nq, a.Nk, n_qblk, a.scale, sl2,
+                       a.diag);
+  }
+  {
+    using C = DkvCfg<D>;
+    const int n_kblk = (a.Nk + C::BK - 1) / C::BK;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)a.B * a.H_kv * n_kblk)),
+                       dim3(C::THREADS), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, (const float*)a.ws, rows, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, group,
+                       a.Nq, a.Nk, n_kblk, a.scale, sl2, a.diag);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return a.causal ? launch_bwd_impl<128, true>(a, stream) : launch_bwd_impl<128, false>(a, stream);
+  return a.causal ? launch_bwd_impl<64, true>(a, stream) : launch_bwd_impl<64, false>(a, stream);
+}
+
+}  // namespace fa

@@ -46,28 +46,10 @@
 //    natural-log units.
 #include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_tile_layout.h"
 
 namespace fa {
 namespace {
-
-// XOR swizzle applied to the 16-byte chunk index of an LDS row, from the row's low 4 bits.
-template <int D> struct Swz;
-template <> struct Swz<128> { static constexpr int b0 = 4, b1 = 10, b2 = 1, b3 = 3; };
-template <> struct Swz<64> { static constexpr int b0 = 2, b1 = 4, b2 = 1, b3 = 3; };
-
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  return ((row & 1) ? Swz<D>::b0 : 0) ^ ((row & 2) ? Swz<D>::b1 : 0) ^
-         ((row & 4) ? Swz<D>::b2 : 0) ^ ((row & 8) ? Swz<D>::b3 : 0);
-}
-
-// The 32x32 MFMA accumulator holds row r = 8*(j/4) + 4*h + (j%4) in register j of lane-half h.
-// key_of_row(r) is the key loaded for row r so that register j of lane-half h is key
-// 16*(j/8) + 8*h + (j%8) of the 32-key block.
-__device__ __forceinline__ int key_of_row(int r) {
-  const int a = r >> 3, h = (r >> 2) & 1, b = r & 3;
-  return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
-}
 
 template <int D>
 struct Bf16Cfg {

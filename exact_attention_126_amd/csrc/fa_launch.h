@@ -40,11 +40,30 @@ struct DecodeCombineArgs {
   int B, H, d, num_splits;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // forward's per-row LSE, natural-log units
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws;  // [2][B][H][Nq]: LSE in log2 units, then rowsum(dO * O)
+  int B, H, Nq, Nk, d;
+  int H_kv;
+  bool causal;
+  int diag;
+  float scale;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_split_bf16(const DecodeSplitArgs& a, hipStream_t stream);
 hipError_t launch_decode_split_f32(const DecodeSplitArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine_bf16(const DecodeCombineArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine_f32(const DecodeCombineArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -56,8 +56,8 @@ typedef enum {
   FA_ERR_ALIGN = 2,       /* q/k/v/o/workspace not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_SHAPE = 3,       /* a size <= 0, H_kv not dividing H, causal with Nq != Nk (fa_fwd) or
                              bottom-right with Nk < Nq, or sizes beyond the index limits */
-  FA_ERR_UNSUPPORTED = 4, /* d not in {64, 128}, or unknown dtype */
-  FA_ERR_WORKSPACE = 5,   /* decode workspace smaller than fa_decode_workspace_bytes() */
+  FA_ERR_UNSUPPORTED = 4, /* d not in {64, 128}, unknown dtype, or fp32 in the backward */
+  FA_ERR_WORKSPACE = 5,   /* workspace smaller than fa_decode_workspace_bytes() / fa_bwd_workspace_bytes() */
   FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
   FA_ERR_ARG = 7          /* scale not finite and > 0, num_splits outside [1, Nk], or an unknown
                              fa_mask_t */
@@ -127,6 +127,30 @@ fa_status_t fa_decode_split_ex(const void* q, const void* k, const void* v,
 fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse,
                               int64_t B, int64_t H, int64_t d, int num_splits,
                               fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Backward pass: the gradients of a loss with respect to q, k and v, given its gradient dout
+ * with respect to the forward's output o.  The probabilities are recomputed tile by tile from
+ * q, k and the forward's lse instead of being stored (M4-047 card "高效注意力与 FlashAttention",
+ * §3 point (c)); with Dr_i = dout_i . o_i:
+ *     P = exp(scale q k^T - lse) (0 where masked),  dv = P^T dout,  dS = P * (dout v^T - Dr),
+ *     dq = scale dS k,  dk = scale dS^T q.
+ *   q, o, dout [B,H,Nq,d]; k, v [B,H_kv,Nk,d]; lse [B,H,Nq] float32 as fa_fwd / fa_fwd_ex wrote
+ *   it for the same q, k, v, mask and scale  (in);
+ *   dq [B,H,Nq,d], dk and dv [B,H_kv,Nk,d]  (out, bf16, RNE; fp32 accumulation inside; the
+ *   gradient of a K/V head sums over the query heads that read it).
+ *   mask, H_kv, scale: as for fa_fwd_ex.  dtype must be FA_DTYPE_BF16.
+ *   workspace: caller-owned device memory of at least fa_bwd_workspace_bytes(B, H, Nq) bytes,
+ *   16-byte aligned; it holds two floats per query row (lse in log2 units and Dr) between the
+ *   launches of one call, and nothing across calls.
+ *   The result is deterministic (no atomics).  Limits as for fa_fwd, and B*H*Nq*8 < 2^31.
+ */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int64_t B, int64_t H, int64_t H_kv, int64_t Nq,
+                   int64_t Nk, int64_t d, fa_mask_t mask, float scale, fa_dtype_t dtype,
+                   hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(fa_status_t status);

@@ -3,7 +3,7 @@
 Recipe (every workload):
   * each (tensor, batch, head) block of shape [rows, d] is drawn independently as
     float32 N(0, 1) from numpy's PCG64 seeded with SeedSequence([seed, tensor_id, b, h]),
-    tensor_id 0 = Q, 1 = K, 2 = V;
+    tensor_id 0 = Q, 1 = K, 2 = V, 3 = dO (the output gradient a backward test feeds in);
   * K is then multiplied by the workload's power-of-two factors (exact in bf16);
   * bf16 workloads round the float32 draw to bf16 with round-to-nearest-even.
 
@@ -21,7 +21,7 @@ import numpy as np
 
 from .workloads import Workload
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}  # "do": the gradient fed to the backward
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -61,7 +61,7 @@ def _apply_k_rule(x: np.ndarray, rule: tuple) -> np.ndarray:
 
 def head_block(w: Workload, which: str, b: int, h: int) -> np.ndarray:
     """One (b, h) block of Q, K or V in storage form ([rows, d] uint16 bf16 bits or float32)."""
-    rows = w.Nq if which == "q" else w.Nk
+    rows = w.Nq if which in ("q", "do") else w.Nk
     x = _draw(w.seed, TENSOR_IDS[which], b, h, rows, w.d)
     if which == "k":
         x = _apply_k_rule(x, w.k_rule)
@@ -79,8 +79,8 @@ def head_block_f32(w: Workload, which: str, b: int, h: int) -> np.ndarray:
 def make_tensor(w: Workload, which: str, threads: int | None = None) -> np.ndarray:
     """Full [B, heads, rows, d] tensor in storage form (heads = H for Q, the K/V head count for
     K and V), heads drawn in parallel."""
-    rows = w.Nq if which == "q" else w.Nk
-    heads = w.H if which == "q" else w.kv_heads
+    rows = w.Nq if which in ("q", "do") else w.Nk
+    heads = w.H if which in ("q", "do") else w.kv_heads
     out = np.empty((w.B, heads, rows, w.d), dtype=np.uint16 if w.dtype == "bf16" else np.float32)
     threads = threads or min(16, len(os.sched_getaffinity(0)))
 

@@ -186,3 +186,26 @@ def test_calibration_library_loads_and_validates():
     assert C.fa_calib_mfma(P_MIS, nb, P, nf, P, 4, 8, None) == -1        # misaligned operands
     assert C.fa_calib_mfma(P, nb, P, nf, P, 4, 6, None) == -1            # niter not a multiple of 4
     assert C.fa_calib_mfma(P, nb, P, nf, P, 0, 8, None) == -1            # empty grid
+
+
+def bwd(L, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, wsb=None, B=1, H=4, H_kv=2, Nq=128, Nk=256, d=128,
+        mask=1, scale=0.1, dtype=BF16):
+    vp = ctypes.c_void_p
+    if wsb is None:
+        wsb = fa.fa_bwd_workspace_bytes(B, H, Nq) if B > 0 and H > 0 and Nq > 0 else 0
+    ptr = lambda x: vp(x) if x else None
+    return L.fa_bwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq), ptr(dk), ptr(dv), ptr(ws), wsb, B, H,
+                    H_kv, Nq, Nk, d, mask, scale, dtype, None)
+
+
+def test_bwd_validation(L):
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 2 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 3, 100) == 0
+    assert bwd(L, do=0) == 1 and bwd(L, ws=0) == 1 and bwd(L, lse=0) == 1
+    assert bwd(L, dtype=F32) == 4 and bwd(L, d=96) == 4
+    assert bwd(L, dk=P_MIS) == 2 and bwd(L, lse=P + 2) == 2 and bwd(L, ws=P + 8) == 2
+    assert bwd(L, mask=5) == 7 and bwd(L, scale=0.0) == 7
+    assert bwd(L, H_kv=3) == 3 and bwd(L, Nq=0) == 3 and bwd(L, mask=2, Nq=300, Nk=200) == 3
+    assert bwd(L, B=2**12, H=2**12, H_kv=2**12, Nq=2**10, wsb=1 << 40) == 3  # workspace offsets beyond 32 bits
+    assert bwd(L, wsb=fa.fa_bwd_workspace_bytes(1, 4, 128) - 4) == 5
+    assert bwd(L) in (0, 6)  # valid: with no GPU in this process the launch reports FA_ERR_HIP
