@@ -240,9 +240,22 @@ struct DkvCfg {
   static constexpr int DB = D / 16;                                    // 16-dim blocks of dK^T, dV^T
 };
 
-// Chunk swizzle of the 32-row Q and dO tiles: the 16 rows a 16-lane group reads at one chunk
-// (and the 4 rows x 4 pieces of a transposing read) spread over the banks.
-__device__ __forceinline__ int qswz(int row) { return row & 7; }
+// Chunk swizzle of the 32-row Q and dO tiles.  A 16-byte read of S or dP has the 16 lanes of a
+// group at rows 8 a + 4 b + c (a = L / 4, c = L % 4, one b) and one chunk; a transposing read has
+// 32 lanes at rows 8 G + 4 I + c (G = 0, 1) and a 32-byte piece each.  At d = 128 (one 256-byte
+// row per bank sweep) the swizzle 2 c + 8 (a & 1) + (a >> 1) gives the 16 lanes 16 different
+// chunks and the 8 rows 8 different 32-byte pieces; at d = 64 (two rows per sweep) the 16-byte
+// reads stay conflict-free and the transposing reads meet at most in pairs.
+template <int D>
+__device__ __forceinline__ int qswz(int row);
+template <>
+__device__ __forceinline__ int qswz<128>(int row) {
+  return 2 * (row & 3) + 8 * ((row >> 3) & 1) + ((row >> 4) & 1);
+}
+template <>
+__device__ __forceinline__ int qswz<64>(int row) {
+  return ((row >> 1) & 1) + 2 * ((row >> 3) & 3);
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
@@ -285,14 +298,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int bl = 0; bl < 2; ++bl) {
     const int row = 8 * (L >> 2) + 4 * bl + (L & 3);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) roff[bl][ks] = row * C::RB + (((4 * ks + G) ^ qswz(row)) << 4);
+    for (int ks = 0; ks < C::KS; ++ks) roff[bl][ks] = row * C::RB + (((4 * ks + G) ^ qswz<D>(row)) << 4);
   }
   // transposing reads for dO^T and Q^T (A of dV^T, dK^T): lane L of group G addresses query
   // 8 G + 4 I + L / 4, dims 16 db + 4 (L % 4) .. + 3 (byte 32 db + 8 (L % 4) of the row); lane l
   // receives dim 16 db + L of queries 8 G + 4 I .. + 3
   auto tr_off = [&](int I, int db) {
     const int row = 8 * G + 4 * I + (L >> 2);
-    return row * C::RB + (((2 * db + ((L & 3) >> 1)) ^ qswz(row)) << 4) + ((L & 1) ? 8 : 0);
+    return row * C::RB + (((2 * db + ((L & 3) >> 1)) ^ qswz<D>(row)) << 4) + ((L & 1) ? 8 : 0);
   };
 
   f32x4v_t dk[C::DB], dv[C::DB];
@@ -320,7 +333,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const int c = x < C::DMAS ? x : x - C::DMAS;
           const int row = c * C::ROWS_PER_DMA + lane / C::CPR;
           const uint32_t off =
-              (uint32_t)min(t * C::BQ + row, Nq - 1) * C::RB + (((lane % C::CPR) ^ qswz(row)) << 4);
+              (uint32_t)min(t * C::BQ + row, Nq - 1) * C::RB + (((lane % C::CPR) ^ qswz<D>(row)) << 4);
           if (x < C::DMAS)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(Qr, (lptr_t)(qb[buf] + c * 1024), 16, off, 0, 0, 0);
           else
