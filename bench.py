@@ -20,10 +20,11 @@ The printed JSON line carries:
   decode       decode KV-read GB/s (K and V read once) with its own HBM roofline
   cpu_baseline the float64 reference implementation timed on the host cores on a sample
                of the same workload (a reported baseline only)
-  extras       the extended entry points, timed separately after the steps (not part of
-               `value`): a bottom-right causal, grouped-K/V-head prefill chunk (fa_fwd_ex,
-               FLOPs counted over the visible query-key pairs) and a grouped-K/V-head decode
-               (fa_decode_split_ex + fa_decode_combine, GB/s of K/V bytes read once)
+  extras       the other entry points, timed separately after the steps (not part of
+               `value`): the backward (fa_bwd) on the headline prefill, a bottom-right causal,
+               grouped-K/V-head prefill chunk (fa_fwd_ex, FLOPs counted over the visible
+               query-key pairs) and a grouped-K/V-head decode (fa_decode_split_ex +
+               fa_decode_combine, GB/s of K/V bytes read once)
 HBM traffic measured with rocprofv3 counters is read from profiles/ when the summary there
 was taken on the current kernel sources, else reported as null.
 """
@@ -192,6 +193,32 @@ def sustained_mfma_ceiling(torch, warm_s: float = 0.3, reps: int = 20) -> dict |
             "operands": "bf16 N(0,1), seeded", "warm_s": warm_s}
 
 
+def time_backward(torch, fa, si, w, dev, o, lse, reps: int = 10) -> dict:
+    """fa_bwd on the headline prefill (its q, k, v and the o, lse of the timed forward) with a seeded
+    N(0,1) dO; TFLOP/s counted as 2.5x the forward's FLOPs (the five products of the gradients
+    against the forward's two), the usual convention, though the kernels compute seven."""
+    stream = torch.cuda.current_stream()
+    do = to_device(w, si.make_tensor(w, "do"))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq) // 4, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
+    mask = fa.FA_MASK_CAUSAL if w.causal else fa.FA_MASK_NONE
+    call = lambda: fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq, dk, dv, ws, mask, w.scale, stream=stream)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.5 * 4.0 * w.B * w.H * w.Nq * w.Nk * w.d / (2 if w.causal else 1) / (ms * 1e-3) / 1e12
+    del do, ws, dq, dk, dv
+    return {"workload": w.name, "entry": "fa_bwd (dQ, dK, dV)", "value": round(tf, 1),
+            "unit": "TFLOP/s (2.5x forward FLOPs)", "ms": round(ms, 4), "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
 def time_extras(torch, fa, si, get, reps: int = 20) -> dict:
     """The extended entry points on their own workloads, each timed over `reps` launches after a
     warm-up, with HIP events on the current stream."""
@@ -340,8 +367,11 @@ def main():
     dec_gbs = kv_bytes / ((ms_split + ms_comb) * 1e-3) / 1e9
     split_gbs = kv_bytes / (ms_split * 1e-3) / 1e9
 
+    bwd = time_backward(torch, fa, si, wp, dp, o, lse) if args.extras == "on" else None
     del dp, dd, o, lse, od, lsed, ws
     extras = time_extras(torch, fa, si, get) if args.extras == "on" else None
+    if extras is not None:
+        extras["backward"] = bwd
     ceiling = sustained_mfma_ceiling(torch) if args.mfma_ceiling == "on" else None
     tr_f = read_traffic("fwd_bf16_prefill_b8h16_n8192_d128_causal_hbm_traffic.txt", FWD_SOURCES)
     tr_d = read_traffic("decode_split_b16h32_nk32768_d128_hbm_traffic.txt", DEC_SOURCES)
