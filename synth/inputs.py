@@ -70,6 +70,43 @@ def head_block(w: Workload, which: str, b: int, h: int) -> np.ndarray:
     return x
 
 
+E4M3_MAX = 448.0  # largest finite OCP FP8 E4M3 value
+
+
+def head_block_fp8(w: Workload, which: str, b: int, h: int):
+    """One (b, h) block of K or V as OCP FP8 E4M3 codes ([rows, d] uint8) and its scale: the
+    float32 draw x (with the K rule) is stored as codes of x / scale, scale = max|x| / 448, rounded
+    to nearest even by torch's float8_e4m3fn conversion.  Input preparation only: the values a
+    kernel and the reference see are the codes and the scale."""
+    import torch
+
+    rows = w.Nk
+    x = _draw(w.seed, TENSOR_IDS[which], b, h, rows, w.d)
+    if which == "k":
+        x = _apply_k_rule(x, w.k_rule)
+    amax = float(np.abs(x).max())
+    scale = np.float32(amax / E4M3_MAX if amax > 0 else 1.0)
+    y = np.clip(x / scale, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, float(scale)
+
+
+def make_kv_fp8(w: Workload, which: str, threads: int | None = None):
+    """Full [B, H_kv, Nk, d] uint8 E4M3 codes of K or V and their [B, H_kv] float32 scales."""
+    heads = w.kv_heads
+    out = np.empty((w.B, heads, w.Nk, w.d), dtype=np.uint8)
+    scales = np.empty((w.B, heads), dtype=np.float32)
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+
+    def fill(bh):
+        b, h = divmod(bh, heads)
+        out[b, h], scales[b, h] = head_block_fp8(w, which, b, h)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(fill, range(w.B * heads)))
+    return out, scales
+
+
 def head_block_f32(w: Workload, which: str, b: int, h: int) -> np.ndarray:
     """Same values as head_block, as float32 (exact for bf16 workloads)."""
     x = head_block(w, which, b, h)

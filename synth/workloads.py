@@ -37,6 +37,8 @@ class Workload:
     num_splits: int = 0  # > 0: decode workload, split-KV into this many partitions
     description: str = ""
     H_kv: int = 0  # K/V heads (0: H); query head h reads K/V head h // (H // H_kv)
+    kv_dtype: str = ""  # "" (as dtype) or "e4m3": K and V stored as OCP FP8 E4M3 codes with a scale per
+    #                     (batch, K/V head)
     causal_align: str = "top_left"  # or "bottom_right": key j visible to row i iff j <= i + Nk - Nq
 
     @property
@@ -90,6 +92,11 @@ WORKLOADS = {
             "decode_gqa_b16h32kv8_nk32768_d128", B=16, H=32, H_kv=8, Nq=1, Nk=32768, d=128, dtype="bf16",
             causal=False, seed=7000, num_splits=64,
             description="1-token decode with four query heads per K/V head, 64-way split-KV + combine"),
+        Workload(
+            "decode_fp8kv_b16h32_nk32768_d128", B=16, H=32, Nq=1, Nk=32768, d=128, dtype="bf16", kv_dtype="e4m3",
+            causal=False, seed=8000, num_splits=64,
+            description="1-token decode against an FP8 (E4M3) KV cache with a scale per (batch, head), "
+                        "64-way split-KV + combine"),
     ]
 }
 
