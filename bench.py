@@ -264,6 +264,26 @@ def time_extras(torch, fa, si, get, reps: int = 20) -> dict:
                          "split_ms": round(ms_s, 4), "combine_ms": round(ms_c, 4),
                          "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
     del dev, ws, o, lse
+    w = get("decode_fp8kv_b16h32_nk32768_d128")
+    q = to_device(w, si.make_tensor(w, "q"))
+    kv = {}
+    for x in "kv":
+        codes, scales = si.make_kv_fp8(w, x)
+        kv[x], kv[x + "s"] = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+        del codes
+    ws = fa.decode_workspace(q, w.num_splits)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, 1), dtype=torch.float32, device="cuda")
+    ms_s = timed(lambda: fa.fa_decode_split_fp8kv(q, kv["k"], kv["v"], kv["ks"], kv["vs"], ws, w.num_splits, w.scale,
+                                                  stream=stream), reps, 3)
+    ms_c = timed(lambda: fa.fa_decode_combine(ws, o, lse, w.num_splits, stream=stream), reps, 3)
+    nbytes = 2.0 * w.B * w.kv_heads * w.Nk * w.d  # one byte per code
+    gbs = nbytes / ((ms_s + ms_c) * 1e-3) / 1e9
+    out["decode_fp8kv"] = {"workload": w.name, "entry": "fa_decode_split_fp8kv + fa_decode_combine (E4M3 K/V)",
+                           "value": round(gbs, 1), "unit": "GB/s (E4M3 K/V bytes read once)",
+                           "split_ms": round(ms_s, 4), "combine_ms": round(ms_c, 4),
+                           "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
+    del q, kv, ws, o, lse
     return out
 
 

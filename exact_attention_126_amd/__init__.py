@@ -27,7 +27,7 @@ FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE", 4: "FA_ERR_UNSUPPORTED",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
 EXPORTED = ["fa_fwd", "fa_fwd_ex", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_split_ex",
-            "fa_decode_combine", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string"]
+            "fa_decode_split_fp8kv", "fa_decode_combine", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string"]
 
 _lib = None
 
@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_ex.restype = i32
         L.fa_decode_split_ex.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32, i32, vp]
         L.fa_decode_split_ex.restype = i32
+        L.fa_decode_split_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32,
+                                            vp]
+        L.fa_decode_split_fp8kv.restype = i32
         L.fa_decode_workspace_bytes.argtypes = [i64, i64, i64, i32]
         L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.fa_decode_split.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, f32, i32, i32, vp]
@@ -188,6 +191,35 @@ def fa_decode_split_ex(q, k, v, workspace, num_splits: int, scale: float | None 
     _raise(st, "fa_decode_split_ex")
 
 
+def fa_decode_split_fp8kv(q, k, v, k_scale, v_scale, workspace, num_splits: int, scale: float | None = None,
+                          stream=None) -> None:
+    """Per-split decode partials over an FP8 KV cache: q [B,H,1,d] bf16, k/v [B,H_kv,Nk,d] E4M3
+    codes (uint8 or float8_e4m3fn), k_scale/v_scale [B,H_kv] float32 (a code's value times its
+    head's scale)."""
+    _check(q, "q", torch.bfloat16)
+    for t, n in ((k, "k"), (v, "v")):
+        _check(t, n)
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must hold E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _check(t, n, torch.float32)
+    _check(workspace, "workspace")
+    _check_shapes(q, k, v, same_heads=False)
+    if q.shape[2] != 1:
+        raise ValueError(f"decode takes one query token per head, q is {tuple(q.shape)}")
+    B, H, _, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.numel() != B * H_kv:
+            raise ValueError(f"{n} must hold B*H_kv = {B * H_kv} scales, has {t.numel()}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_decode_split_fp8kv(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), B, H, H_kv, Nk, d, float(scale),
+                                     int(num_splits), _stream(stream))
+    _raise(st, "fa_decode_split_fp8kv")
+
+
 def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None) -> None:
     """Merge the split partials into o [B,H,1,d] and lse [B,H,1]."""
     _check(workspace, "workspace")
@@ -258,6 +290,20 @@ def decode(q, k, v, num_splits: int, scale: float | None = None, workspace=None,
         fa_decode_split(q, k, v, workspace, num_splits, scale, stream)
     else:
         fa_decode_split_ex(q, k, v, workspace, num_splits, scale, stream)
+    fa_decode_combine(workspace, o, lse, num_splits, stream)
+    return o, lse
+
+
+def decode_fp8kv(q, k, v, k_scale, v_scale, num_splits: int, scale: float | None = None, workspace=None,
+                 stream=None):
+    """(o, lse) of one-token decode over an FP8 KV cache: fa_decode_split_fp8kv then
+    fa_decode_combine (bf16 o) on the same stream."""
+    B, H, _, d = q.shape
+    if workspace is None:
+        workspace = decode_workspace(q, num_splits)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    fa_decode_split_fp8kv(q, k, v, k_scale, v_scale, workspace, num_splits, scale, stream)
     fa_decode_combine(workspace, o, lse, num_splits, stream)
     return o, lse
 

@@ -118,6 +118,28 @@ fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, voi
                                          : fa::launch_decode_combine_f32(a, stream));
 }
 
+fa_status_t fa_decode_split_fp8kv(const void* q, const void* k, const void* v, const float* k_scale,
+                                  const float* v_scale, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                                  int64_t H_kv, int64_t Nk, int64_t d, float scale, int num_splits,
+                                  hipStream_t stream) {
+  if (!q || !k || !v || !k_scale || !v_scale || !workspace) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(workspace, 16) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4))
+    return FA_ERR_ALIGN;
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Nk <= 0 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (Nk > kI32Max / d || B > kI32Max / H) return FA_ERR_SHAPE;  // one head of codes: 32-bit offsets
+  if (num_splits < 1 || num_splits > Nk || !scale_ok(scale)) return FA_ERR_ARG;
+  if (B * H > kI32Max / num_splits) return FA_ERR_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  float* o_part = static_cast<float*>(workspace);
+  float* ml = o_part + (size_t)(B * H * num_splits) * (size_t)d;
+  fa::DecodeSplitFp8Args a{q, k, v, k_scale, v_scale, o_part, ml, (int)B, (int)H, (int)Nk, (int)d, num_splits,
+                           (int)H_kv, scale};
+  return from_hip(fa::launch_decode_split_fp8kv(a, stream));
+}
+
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
   if (B <= 0 || H <= 0 || Nq <= 0 || B > kI32Max / H || B * H > kI32Max / Nq) return 0;
   return (size_t)(B * H * Nq) * 2 * sizeof(float);

@@ -31,12 +31,12 @@ constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
 
-// Sum over aligned groups of W consecutive lanes (W in {8, 16, 32}); every lane gets the sum.
+// Sum over aligned groups of W consecutive lanes (W in {4, 8, 16, 32}); every lane gets the sum.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
   x += dpp<kQuadSwap1>(x);
   x += dpp<kQuadSwap2>(x);
-  x += dpp<kRowHalfMirror>(x);  // pairs quad 0 with quad 1 of each 8 lanes
+  if (W >= 8) x += dpp<kRowHalfMirror>(x);  // pairs quad 0 with quad 1 of each 8 lanes
   if (W >= 16) x += dpp<kRowMirror>(x);  // pairs the two 8-lane halves of each row
   if (W >= 32) x += __shfl_xor(x, 16);
   return x;
@@ -199,6 +199,162 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
   }
 }
 
+// Decode split over an FP8 KV cache: K and V rows are OCP E4M3 codes (one byte per element)
+// with one float scale per (batch, K/V head), the value of a code being its E4M3 value times the
+// scale (KV-cache quantisation, which the Day-21 page's FAQ Q5 names among the decode-side
+// techniques: the cache is read with half the bytes of bf16).  Same structure as
+// decode_split_kernel: D/16 lanes share a key row (16 codes per lane, one 16-byte load), widened to
+// fp32 two at a time by v_cvt_pk_f32_fp8; the K scale is folded into q once and the V scale into
+// the partial output.  Queries are bf16 and the partials fp32, so fa_decode_combine is unchanged.
+template <int D, int GE>
+__global__ __launch_bounds__(256) void decode_split_fp8_kernel(const uint16_t* __restrict__ Q,
+                                                               const uint8_t* __restrict__ K,
+                                                               const uint8_t* __restrict__ V,
+                                                               const float* __restrict__ Ks,
+                                                               const float* __restrict__ Vs,
+                                                               float* __restrict__ Opart, float* __restrict__ ML,
+                                                               int Nk, int S, int chunk, float sl2, int H, int group) {
+  constexpr int EPL = 16;         // codes per lane per key row
+  constexpr int LPK = D / EPL;    // lanes per key row
+  constexpr int KPW = 64 / LPK;   // key rows per wave per step
+  constexpr int U = 4;            // steps in flight per iteration
+  constexpr int WAVES = 4;
+  __shared__ float s_m[WAVES][GE], s_l[WAVES][GE];
+  __shared__ float s_acc[WAVES][GE][D];
+
+  const int s = blockIdx.x % S;
+  const int bh0 = (blockIdx.x / S) * GE;
+  const int start = s * chunk;
+  const int end = min(Nk, start + chunk);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int gi = lane / LPK, li = lane % LPK;
+  const int kvh = (bh0 / H) * (H / group) + (bh0 % H) / group;
+  const float ks = Ks[kvh], vs = Vs[kvh];
+
+  float qv[GE][EPL];
+#pragma unroll
+  for (int g = 0; g < GE; ++g) {
+    const uint16_t* qp = Q + (int64_t)(bh0 + g) * D + li * EPL;
+    Elt<uint16_t>::widen(gload16(qp), qv[g]);
+    Elt<uint16_t>::widen(gload16(qp + 8), qv[g] + 8);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[g][e] *= ks;
+  }
+  const uint8_t* Kh = K + (int64_t)kvh * Nk * D + li * EPL;
+  const uint8_t* Vh = V + (int64_t)kvh * Nk * D + li * EPL;
+  auto widen8 = [](u32x4_t r, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r[i], true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  };
+
+  float m[GE], l[GE], acc[GE][EPL];
+#pragma unroll
+  for (int g = 0; g < GE; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  for (int base = start + wave * U * KPW; base < end; base += WAVES * U * KPW) {
+    u32x4_t kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = min(base + u * KPW + gi, end - 1);
+      kr[u] = gload16(Kh + (int64_t)key * D);
+      vr[u] = gload16(Vh + (int64_t)key * D);
+    }
+    float sc[U][GE];
+    float bm[GE];
+#pragma unroll
+    for (int g = 0; g < GE; ++g) bm[g] = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[EPL];
+      widen8(kr[u], kf);
+      const bool in = base + u * KPW + gi < end;
+#pragma unroll
+      for (int g = 0; g < GE; ++g) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[g][e], kf[e], dot);
+        dot = group_sum<LPK>(dot);
+        sc[u][g] = in ? dot * sl2 : -INFINITY;
+        bm[g] = fmaxf(bm[g], sc[u][g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GE; ++g) {
+#pragma unroll
+      for (int w = LPK; w < 64; w <<= 1) bm[g] = fmaxf(bm[g], __shfl_xor(bm[g], w));
+      const float mnew = fmaxf(m[g], bm[g]);
+      const float alpha = fast_exp2(m[g] - mnew);
+      m[g] = mnew;
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[EPL];
+      widen8(vr[u], vf);
+#pragma unroll
+      for (int g = 0; g < GE; ++g) {
+        const float p = fast_exp2(sc[u][g] - m[g]);
+        l[g] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = __builtin_fmaf(p, vf[e], acc[g][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < GE; ++g) {
+#pragma unroll
+    for (int w = LPK; w < 64; w <<= 1) {
+      l[g] += __shfl_xor(l[g], w);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], w);
+    }
+    if (lane == 0) {
+      s_m[wave][g] = m[g];
+      s_l[wave][g] = l[g];
+    }
+    if (gi == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][g][li * EPL + e] = acc[g][e];
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < GE * D; x += 256) {
+    const int g = x / D, dim = x % D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, s_m[w][g]);
+    float o = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float f = fast_exp2(s_m[w][g] - M);
+        o = __builtin_fmaf(f, s_acc[w][g][dim], o);
+        L = __builtin_fmaf(f, s_l[w][g], L);
+      }
+    }
+    const int64_t rec = (int64_t)(bh0 + g) * S + s;
+    Opart[rec * D + dim] = o * vs;
+    if (dim == 0) {
+      ML[rec * 2] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+      ML[rec * 2 + 1] = L;
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ Opart,
                                                              const float* __restrict__ ML, T* __restrict__ O,
@@ -261,7 +417,36 @@ hipError_t combine_impl(const DecodeCombineArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int GE>
+void launch_split_fp8(const DecodeSplitFp8Args& a, int chunk, float sl2, hipStream_t stream) {
+  const int64_t nblk = (int64_t)a.B * (a.H / GE) * a.num_splits;
+  hipLaunchKernelGGL((decode_split_fp8_kernel<D, GE>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                     (const uint16_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.k_scale, a.v_scale, a.o_part,
+                     a.ml, a.Nk, a.num_splits, chunk, sl2, a.H, a.H / a.H_kv);
+}
+
+template <int D>
+void launch_split_fp8_d(const DecodeSplitFp8Args& a, int chunk, float sl2, hipStream_t stream) {
+  const int group = a.H / a.H_kv;
+  if (group % 4 == 0)
+    launch_split_fp8<D, 4>(a, chunk, sl2, stream);
+  else if (group % 2 == 0)
+    launch_split_fp8<D, 2>(a, chunk, sl2, stream);
+  else
+    launch_split_fp8<D, 1>(a, chunk, sl2, stream);
+}
+
 }  // namespace
+
+hipError_t launch_decode_split_fp8kv(const DecodeSplitFp8Args& a, hipStream_t stream) {
+  const int chunk = (a.Nk + a.num_splits - 1) / a.num_splits;
+  const float sl2 = a.scale * kLog2e;
+  if (a.d == 128)
+    launch_split_fp8_d<128>(a, chunk, sl2, stream);
+  else
+    launch_split_fp8_d<64>(a, chunk, sl2, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_split_bf16(const DecodeSplitArgs& a, hipStream_t stream) { return split_impl<uint16_t>(a, stream); }
 hipError_t launch_decode_split_f32(const DecodeSplitArgs& a, hipStream_t stream) { return split_impl<float>(a, stream); }

@@ -32,6 +32,19 @@ struct DecodeSplitArgs {
   float scale;
 };
 
+struct DecodeSplitFp8Args {
+  const void* q;        // bf16 [B][H][1][d]
+  const void* k;        // E4M3 codes [B][H_kv][Nk][d]
+  const void* v;
+  const float* k_scale;  // [B][H_kv]
+  const float* v_scale;
+  float* o_part;
+  float* ml;
+  int B, H, Nk, d, num_splits;
+  int H_kv;
+  float scale;
+};
+
 struct DecodeCombineArgs {
   const float* o_part;
   const float* ml;
@@ -65,5 +78,6 @@ hipError_t launch_decode_split_f32(const DecodeSplitArgs& a, hipStream_t stream)
 hipError_t launch_decode_combine_bf16(const DecodeCombineArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine_f32(const DecodeCombineArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_decode_split_fp8kv(const DecodeSplitFp8Args& a, hipStream_t stream);
 
 }  // namespace fa

@@ -129,6 +129,21 @@ fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, voi
                               fa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Split step of decode against an FP8 KV cache (KV-cache quantisation, which the Day-21 page's
+ * FAQ Q5 names among the decode-side techniques; the cache is read with half the bytes of bf16):
+ *   q [B,H,1,d] bf16; k and v [B,H_kv,Nk,d] OCP FP8 E4M3 codes, one byte per element (sign,
+ *   4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinity, S.1111.111 = NaN);
+ *   k_scale and v_scale [B,H_kv] float32: the value of a code of K/V head (b, j) is its E4M3
+ *   value times k_scale[b*H_kv + j] (resp. v_scale).  Everything else (grouped heads, splits, the
+ *   workspace and its size, errors) is as for fa_decode_split_ex; fa_decode_combine with dtype
+ *   FA_DTYPE_BF16 merges the partials into a bf16 o.  NaN codes give NaN results.
+ */
+fa_status_t fa_decode_split_fp8kv(const void* q, const void* k, const void* v, const float* k_scale,
+                                  const float* v_scale, void* workspace, size_t workspace_bytes,
+                                  int64_t B, int64_t H, int64_t H_kv, int64_t Nk, int64_t d,
+                                  float scale, int num_splits, hipStream_t stream);
+
+/*
  * Backward pass: the gradients of a loss with respect to q, k and v, given its gradient dout
  * with respect to the forward's output o.  The probabilities are recomputed tile by tile from
  * q, k and the forward's lse instead of being stored (M4-047 card "高效注意力与 FlashAttention",

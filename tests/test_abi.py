@@ -114,6 +114,25 @@ def test_decode_split_ex_validation(L):
     assert split_ex(L, wsb=fa.fa_decode_workspace_bytes(2, 4, 128, 4) - 1) == 5
 
 
+def split_fp8(L, q=P, k=P, v=P, ks=P, vs=P, ws=P, wsb=None, B=2, H=4, H_kv=2, Nk=100, d=128, scale=0.1, S=4):
+    vp = ctypes.c_void_p
+    if wsb is None:
+        wsb = fa.fa_decode_workspace_bytes(B, H, d, S) if S > 0 else 0
+    ptr = lambda x: vp(x) if x else None  # noqa: E731
+    return L.fa_decode_split_fp8kv(ptr(q), ptr(k), ptr(v), ptr(ks), ptr(vs), ptr(ws), wsb, B, H, H_kv, Nk, d, scale,
+                                   S, None)
+
+
+def test_decode_split_fp8kv_validation(L):
+    assert split_fp8(L, ks=0) == 1 and split_fp8(L, vs=0) == 1 and split_fp8(L, k=0) == 1
+    assert split_fp8(L, d=96) == 4
+    assert split_fp8(L, v=P_MIS) == 2 and split_fp8(L, ks=P + 2) == 2
+    assert split_fp8(L, H_kv=0) == 3 and split_fp8(L, H_kv=3) == 3 and split_fp8(L, Nk=0) == 3
+    assert split_fp8(L, S=0, wsb=1 << 20) == 7 and split_fp8(L, S=101) == 7
+    assert split_fp8(L, scale=float("nan")) == 7
+    assert split_fp8(L, wsb=fa.fa_decode_workspace_bytes(2, 4, 128, 4) - 1) == 5
+
+
 def test_decode_workspace_bytes(L):
     assert fa.fa_decode_workspace_bytes(16, 32, 128, 64) == 16 * 32 * 64 * 130 * 4
     assert fa.fa_decode_workspace_bytes(0, 32, 128, 64) == 0
