@@ -15,7 +15,7 @@ Modules:
   recurrence  - the online-softmax block recurrence in pure Python (tiny inputs only),
                 used to pin the block-by-block steps against the two-pass definition.
   backward    - the gradients dQ, dK, dV by the chain rule through the same definition.
-  fp8         - OCP FP8 E4M3 values and attention over an FP8 KV cache.
+  fp8         - OCP FP8 E4M3 values and attention over FP8 inputs (KV cache; Q, K, V).
 
 Every function here is pinned by tests marked "not gpu" (closed forms, invariants,
 library special cases, brute force and the pages' own worked example).
@@ -25,5 +25,5 @@ from .attention import (  # noqa: F401
     split_bounds, split_partials, combine_partials,
 )
 from .backward import attention_backward_head, attention_backward, softmax_row_stat  # noqa: F401
-from .fp8 import e4m3_value, e4m3_decode, attention_head_fp8kv  # noqa: F401
+from .fp8 import e4m3_value, e4m3_decode, attention_head_fp8kv, attention_head_fp8  # noqa: F401
 from . import recurrence  # noqa: F401

@@ -74,13 +74,13 @@ E4M3_MAX = 448.0  # largest finite OCP FP8 E4M3 value
 
 
 def head_block_fp8(w: Workload, which: str, b: int, h: int):
-    """One (b, h) block of K or V as OCP FP8 E4M3 codes ([rows, d] uint8) and its scale: the
+    """One (b, h) block of Q, K or V as OCP FP8 E4M3 codes ([rows, d] uint8) and its scale: the
     float32 draw x (with the K rule) is stored as codes of x / scale, scale = max|x| / 448, rounded
     to nearest even by torch's float8_e4m3fn conversion.  Input preparation only: the values a
     kernel and the reference see are the codes and the scale."""
     import torch
 
-    rows = w.Nk
+    rows = w.Nq if which in ("q", "do") else w.Nk
     x = _draw(w.seed, TENSOR_IDS[which], b, h, rows, w.d)
     if which == "k":
         x = _apply_k_rule(x, w.k_rule)
@@ -92,9 +92,11 @@ def head_block_fp8(w: Workload, which: str, b: int, h: int):
 
 
 def make_kv_fp8(w: Workload, which: str, threads: int | None = None):
-    """Full [B, H_kv, Nk, d] uint8 E4M3 codes of K or V and their [B, H_kv] float32 scales."""
-    heads = w.kv_heads
-    out = np.empty((w.B, heads, w.Nk, w.d), dtype=np.uint8)
+    """Full [B, heads, rows, d] uint8 E4M3 codes of Q, K or V and their [B, heads] float32 scales
+    (heads = H and rows = Nq for Q; the K/V head count and Nk for K and V)."""
+    heads = w.H if which in ("q", "do") else w.kv_heads
+    rows = w.Nq if which in ("q", "do") else w.Nk
+    out = np.empty((w.B, heads, rows, w.d), dtype=np.uint8)
     scales = np.empty((w.B, heads), dtype=np.float32)
     threads = threads or min(16, len(os.sched_getaffinity(0)))
 

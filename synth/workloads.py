@@ -39,6 +39,7 @@ class Workload:
     H_kv: int = 0  # K/V heads (0: H); query head h reads K/V head h // (H // H_kv)
     kv_dtype: str = ""  # "" (as dtype) or "e4m3": K and V stored as OCP FP8 E4M3 codes with a scale per
     #                     (batch, K/V head)
+    q_dtype: str = ""  # "" (as dtype) or "e4m3": Q stored as E4M3 codes with a scale per (batch, head)
     causal_align: str = "top_left"  # or "bottom_right": key j visible to row i iff j <= i + Nk - Nq
 
     @property
@@ -97,6 +98,11 @@ WORKLOADS = {
             causal=False, seed=8000, num_splits=64,
             description="1-token decode against an FP8 (E4M3) KV cache with a scale per (batch, head), "
                         "64-way split-KV + combine"),
+        Workload(
+            "prefill_fp8_b8h16_n8192_d128_causal", B=8, H=16, Nq=8192, Nk=8192, d=128, dtype="bf16",
+            kv_dtype="e4m3", q_dtype="e4m3", causal=True, seed=9000, k_rule=("scale_all", 2.0),
+            description="the headline causal prefill with Q, K and V as FP8 (E4M3) codes, a scale per "
+                        "(batch, head) and tensor; O in bf16"),
     ]
 }
 
