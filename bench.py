@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP/clk
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PREFILL = "prefill_b8h16_n8192_d128_causal"
 DECODE = "decode_b16h32_nk32768_d128"
@@ -264,6 +265,23 @@ def time_extras(torch, fa, si, get, reps: int = 20) -> dict:
                          "split_ms": round(ms_s, 4), "combine_ms": round(ms_c, 4),
                          "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
     del dev, ws, o, lse
+    w = get("prefill_fp8_b8h16_n8192_d128_causal")
+    t8 = {}
+    for x in "qkv":
+        codes, scales = si.make_kv_fp8(w, x)
+        t8[x], t8[x + "s"] = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+        del codes
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: fa.fa_fwd_fp8(t8["q"], t8["k"], t8["v"], t8["qs"], t8["ks"], t8["vs"], o, lse,
+                                     fa.FA_MASK_CAUSAL, w.scale, stream=stream), reps, 3)
+    flops = 4.0 * w.B * w.H * w.d * (w.Nq * (w.Nq + 1) / 2)  # visible (query, key) pairs, 4d FLOP each
+    tf = flops / (ms * 1e-3) / 1e12
+    out["prefill_fp8"] = {"workload": w.name, "entry": "fa_fwd_fp8 (E4M3 Q, K, V; causal)", "value": round(tf, 1),
+                          "unit": "TFLOP/s", "ms": round(ms, 4),
+                          "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+                          "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    del t8, o, lse
     w = get("decode_fp8kv_b16h32_nk32768_d128")
     q = to_device(w, si.make_tensor(w, "q"))
     kv = {}

@@ -26,7 +26,7 @@ MASKS = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "causal_bottom_right": 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE", 4: "FA_ERR_UNSUPPORTED",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
-EXPORTED = ["fa_fwd", "fa_fwd_ex", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_split_ex",
+EXPORTED = ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_split_ex",
             "fa_decode_split_fp8kv", "fa_decode_combine", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string"]
 
 _lib = None
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_ex.restype = i32
         L.fa_decode_split_ex.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32, i32, vp]
         L.fa_decode_split_ex.restype = i32
+        L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, f32, vp]
+        L.fa_fwd_fp8.restype = i32
         L.fa_decode_split_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32,
                                             vp]
         L.fa_decode_split_fp8kv.restype = i32
@@ -152,6 +154,35 @@ def fa_fwd_ex(q, k, v, o, lse, mask=FA_MASK_NONE, scale: float | None = None, st
     _raise(st, "fa_fwd_ex")
 
 
+def _check_codes(t, name):
+    _check(t, name)
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+
+
+def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, mask=FA_MASK_NONE, scale: float | None = None,
+               stream=None) -> None:
+    """Forward with FP8 inputs: q [B,H,Nq,d], k/v [B,H_kv,Nk,d] E4M3 codes; q_scale [B,H] and
+    k_scale/v_scale [B,H_kv] float32; o [B,H,Nq,d] bf16 and lse [B,H,Nq] float32 out."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_codes(t, n)
+    _check(o, "o", torch.bfloat16)
+    _check(lse, "lse", torch.float32)
+    _check_shapes(q, k, v, o, lse, same_heads=False)
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    for t, n, cnt in ((q_scale, "q_scale", B * H), (k_scale, "k_scale", B * H_kv), (v_scale, "v_scale", B * H_kv)):
+        _check(t, n, torch.float32)
+        if t.numel() != cnt:
+            raise ValueError(f"{n} must hold {cnt} scales, has {t.numel()}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    m = MASKS[mask] if isinstance(mask, str) else int(mask)
+    st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o), _ptr(lse),
+                          B, H, H_kv, Nq, Nk, d, m, float(scale), _stream(stream))
+    _raise(st, "fa_fwd_fp8")
+
+
 def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
     return int(lib().fa_decode_workspace_bytes(B, H, d, num_splits))
 
@@ -198,9 +229,7 @@ def fa_decode_split_fp8kv(q, k, v, k_scale, v_scale, workspace, num_splits: int,
     head's scale)."""
     _check(q, "q", torch.bfloat16)
     for t, n in ((k, "k"), (v, "v")):
-        _check(t, n)
-        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
-            raise TypeError(f"{n} must hold E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+        _check_codes(t, n)
     for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
         _check(t, n, torch.float32)
     _check(workspace, "workspace")
@@ -270,6 +299,15 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=
     else:
         fa_fwd_ex(q, k, v, o, lse, (FA_MASK_CAUSAL if causal else FA_MASK_NONE) if mask is None else mask, scale,
                   stream)
+    return o, lse
+
+
+def attention_fp8(q, k, v, q_scale, k_scale, v_scale, mask=FA_MASK_NONE, scale: float | None = None, stream=None):
+    """(o, lse) = fa_fwd_fp8 on E4M3 codes with their per-head scales; o is bf16."""
+    B, H, Nq, d = q.shape
+    o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, mask, scale, stream)
     return o, lse
 
 

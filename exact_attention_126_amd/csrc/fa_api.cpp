@@ -83,6 +83,31 @@ fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, floa
   return forward(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, mask, false, scale, dtype, stream);
 }
 
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, const float* k_scale,
+                       const float* v_scale, void* o, float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t Nq,
+                       int64_t Nk, int64_t d, fa_mask_t mask, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_CAUSAL_BOTTOM_RIGHT) return FA_ERR_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return FA_ERR_ALIGN;
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Nq <= 0 || Nk <= 0 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (mask == FA_MASK_CAUSAL_BOTTOM_RIGHT && Nk < Nq) return FA_ERR_SHAPE;
+  if (!head_fits(Nq, d, FA_DTYPE_BF16) || Nk > kI32Max / d) return FA_ERR_SHAPE;  // o in bf16, k/v one byte
+  if (B > kI32Max / H || B * H > kI32Max / ((Nq + 31) / 32)) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_ARG;
+  int dev = 0, num_cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cus <= 0)
+    return FA_ERR_HIP;
+  const bool causal = mask != FA_MASK_NONE;
+  const int diag = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT ? (int)(Nk - Nq) : 0;
+  fa::FwdFp8Args a{q, k, v, q_scale, k_scale, v_scale, o, lse, (int)B, (int)H, (int)Nq, (int)Nk, (int)d, (int)H_kv,
+                   causal, diag, scale, num_cus};
+  return from_hip(fa::launch_fwd_fp8(a, stream));
+}
+
 size_t fa_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int num_splits) {
   if (B <= 0 || H <= 0 || d <= 0 || num_splits <= 0) return 0;
   if (B > kI32Max / H || B * H > kI32Max / num_splits) return 0;

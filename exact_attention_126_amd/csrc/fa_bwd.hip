@@ -30,12 +30,6 @@ namespace fa {
 namespace {
 
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // ------------------------------------------------------------------ preprocess
 // One 16-lane group per query row: Dr = dO . O (fp32 sum of bf16 products), L2 = LSE * log2 e.

@@ -72,4 +72,24 @@ __device__ __forceinline__ i16x4_t lds_load8_tr16(const FA_LDS char* p) {
 
 __device__ __forceinline__ u32x4_t gload16(const void* p) { return *(const u32x4_t*)p; }
 
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Raw buffer resource over the bytes [base, base + bytes).  Word 3 selects the 32-bit data format:
+// untyped buffer accesses need a non-zero format on this architecture.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time loop).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 }  // namespace fa

@@ -78,26 +78,6 @@ constexpr float kLazyRescale = 8.f;
 #define FA_LOOKAHEAD 8  // MFMAs by which LDS operand reads run ahead
 #endif
 
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-// Raw buffer resource over the bytes [base, base + bytes).  Word 3 selects the 32-bit data format:
-// untyped buffer accesses need a non-zero format on this architecture.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time loop).
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Eight waves: group 0 (waves 0-3) and group 1 (waves 4-7) each cover the four SIMDs, so every
 // SIMD runs one wave of each group.  Time is cut into half-periods separated by workgroup
 // barriers.  In half-period h a wave of group g works on phase p = h - g:

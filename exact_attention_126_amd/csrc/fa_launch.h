@@ -21,6 +21,23 @@ struct FwdArgs {
   int num_cus;  // compute units of the device the stream runs on (persistent grid size)
 };
 
+struct FwdFp8Args {
+  const void* q;  // E4M3 codes [B][H][Nq][d]
+  const void* k;  // E4M3 codes [B][H_kv][Nk][d]
+  const void* v;
+  const float* q_scale;  // [B][H]
+  const float* k_scale;  // [B][H_kv]
+  const float* v_scale;
+  void* o;  // bf16 [B][H][Nq][d]
+  float* lse;
+  int B, H, Nq, Nk, d;
+  int H_kv;
+  bool causal;
+  int diag;
+  float scale;
+  int num_cus;
+};
+
 struct DecodeSplitArgs {
   const void* q;
   const void* k;
@@ -79,5 +96,6 @@ hipError_t launch_decode_combine_bf16(const DecodeCombineArgs& a, hipStream_t st
 hipError_t launch_decode_combine_f32(const DecodeCombineArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_split_fp8kv(const DecodeSplitFp8Args& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream);
 
 }  // namespace fa

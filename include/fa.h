@@ -90,6 +90,24 @@ fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, floa
                       fa_mask_t mask, float scale, fa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Forward with FP8 inputs (the Day-21 page names FP8 as a FlashAttention-3 feature at the close of
+ * its §6): q [B,H,Nq,d], k and v [B,H_kv,Nk,d] are OCP FP8 E4M3 codes, one byte per element
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinity, S.1111.111 =
+ * NaN); q_scale [B,H], k_scale and v_scale [B,H_kv] float32: an element's value is the E4M3 value
+ * of its code times the scale of its (batch, head).  o [B,H,Nq,d] bf16 and lse [B,H,Nq] float32
+ * (out), as fa_fwd_ex computes them on the decoded values: O = softmax(scale * Q K^T) V with the
+ * mask, LSE natural log.  Both products run on the FP8 matrix core; P is rounded to E4M3 (round
+ * to nearest even) for the second, with values kept between 2^-10 and 2^8 of the running row
+ * max so that none but the negligible ones fall into the E4M3 subnormals; the row sums and LSE
+ * use the unrounded P.  Grouped heads, masks, layouts, limits and errors as for fa_fwd_ex
+ * (q, k, v, o 16-byte aligned; the scales and lse 4-byte aligned).
+ */
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                       const float* k_scale, const float* v_scale, void* o, float* lse, int64_t B,
+                       int64_t H, int64_t H_kv, int64_t Nq, int64_t Nk, int64_t d, fa_mask_t mask,
+                       float scale, hipStream_t stream);
+
+/*
  * Split-KV decode (one query token per (b, h) against a KV cache): the keys are split into
  * num_splits contiguous chunks of ceil(Nk / num_splits) keys that are processed in parallel,
  * then the partial results are merged (Q31 answer, "FlashAttention 为什么快", follow-up 3;

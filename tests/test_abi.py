@@ -133,6 +133,24 @@ def test_decode_split_fp8kv_validation(L):
     assert split_fp8(L, wsb=fa.fa_decode_workspace_bytes(2, 4, 128, 4) - 1) == 5
 
 
+def fwd_fp8(L, q=P, k=P, v=P, qs=P, ks=P, vs=P, o=P, lse=P, B=2, H=4, H_kv=2, Nq=100, Nk=100, d=128, mask=0,
+            scale=0.1):
+    vp = ctypes.c_void_p
+    ptr = lambda x: vp(x) if x else None  # noqa: E731
+    return L.fa_fwd_fp8(ptr(q), ptr(k), ptr(v), ptr(qs), ptr(ks), ptr(vs), ptr(o), ptr(lse), B, H, H_kv, Nq, Nk, d,
+                        mask, scale, None)
+
+
+def test_fwd_fp8_validation(L):
+    assert fwd_fp8(L, qs=0) == 1 and fwd_fp8(L, vs=0) == 1 and fwd_fp8(L, lse=0) == 1
+    assert fwd_fp8(L, mask=3) == 7 and fwd_fp8(L, scale=0.0) == 7
+    assert fwd_fp8(L, d=32) == 4
+    assert fwd_fp8(L, o=P_MIS) == 2 and fwd_fp8(L, ks=P + 1) == 2
+    assert fwd_fp8(L, H_kv=3) == 3 and fwd_fp8(L, Nq=0) == 3
+    assert fwd_fp8(L, mask=2, Nq=200, Nk=100) == 3
+    assert fwd_fp8(L, Nk=(1 << 31) // 128 + 1) == 3
+
+
 def test_decode_workspace_bytes(L):
     assert fa.fa_decode_workspace_bytes(16, 32, 128, 64) == 16 * 32 * 64 * 130 * 4
     assert fa.fa_decode_workspace_bytes(0, 32, 128, 64) == 0
