@@ -345,11 +345,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     };
 
-    if (q_first < n_qt) issue(q_first, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    for (int t = q_first; t < n_qt; ++t) {
-      const int cur = (t - q_first) & 1;
+    // One 32-query tile with its LDS slot fixed at compile time (the loop below alternates the
+    // two), so every LDS address is a per-lane base plus an immediate.  Only tiles that reach past
+    // the wave's diagonal or the end of the queries are masked element by element.
+    auto tile = [&](int t, auto slot) {
+      constexpr int cur = decltype(slot)::value;
       if (t + 1 < n_qt) issue(t + 1, cur ^ 1);
       const FA_LDS char* qt = (const FA_LDS char*)qb[cur];
       const FA_LDS char* ot = (const FA_LDS char*)ob[cur];
@@ -373,26 +373,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const f32x4v_t l2b = *(const FA_LDS f32x4v_t*)(st + 8 * G + 4);
       const f32x4v_t dra = *(const FA_LDS f32x4v_t*)(st + C::BQ + 8 * G);
       const f32x4v_t drb = *(const FA_LDS f32x4v_t*)(st + C::BQ + 8 * G + 4);
+      const bool masked = (q0 + C::BQ > Nq) || (CAUSAL && k0 + wave * 16 + 15 > q0 + diag);
       u32x4_t pB, dsB;
+      auto p_ds = [&](auto mask_tag) {
 #pragma unroll
-      for (int bl = 0; bl < 2; ++bl)
+        for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
-        for (int j2 = 0; j2 < 2; ++j2) {
-          float pv[2], dsv[2];
+          for (int j2 = 0; j2 < 2; ++j2) {
+            float pv[2], dsv[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int j = 2 * j2 + e;
-            const int qq = q0 + 8 * G + 4 * bl + j;
-            const float l2 = bl ? l2b[j] : l2a[j];
-            const float dr = bl ? drb[j] : dra[j];
-            float p = fast_exp2(__builtin_fmaf(s[bl][j], sl2, -l2));
-            if (qq >= Nq || (CAUSAL && key > qq + diag)) p = 0.f;
-            pv[e] = p;
-            dsv[e] = p * (dp[bl][j] - dr);
+            for (int e = 0; e < 2; ++e) {
+              const int j = 2 * j2 + e;
+              const float l2 = bl ? l2b[j] : l2a[j];
+              const float dr = bl ? drb[j] : dra[j];
+              float p = fast_exp2(__builtin_fmaf(s[bl][j], sl2, -l2));
+              if constexpr (decltype(mask_tag)::value) {
+                const int qq = q0 + 8 * G + 4 * bl + j;
+                if (qq >= Nq || (CAUSAL && key > qq + diag)) p = 0.f;
+              }
+              pv[e] = p;
+              dsv[e] = p * (dp[bl][j] - dr);
+            }
+            pB[2 * bl + j2] = pack_bf16x2(pv[0], pv[1]);
+            dsB[2 * bl + j2] = pack_bf16x2(dsv[0], dsv[1]);
           }
-          pB[2 * bl + j2] = pack_bf16x2(pv[0], pv[1]);
-          dsB[2 * bl + j2] = pack_bf16x2(dsv[0], dsv[1]);
-        }
+      };
+      if (masked)
+        p_ds(std::true_type{});
+      else
+        p_ds(std::false_type{});
       // dV^T += dO^T P,  dK^T += Q^T dS  (k = the tile's 32 queries)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
@@ -407,7 +416,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
+    };
+
+    if (q_first < n_qt) issue(q_first, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    int t = q_first;
+    for (; t + 1 < n_qt; t += 2) {
+      tile(t, std::integral_constant<int, 0>{});
+      tile(t + 1, std::integral_constant<int, 1>{});
     }
+    if (t < n_qt) tile(t, std::integral_constant<int, 0>{});
   }
 
   // dK = scale dK^T^T, dV = dV^T^T: register j of block db is dim 16 db + 4 G + j of key `key`
