@@ -156,11 +156,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int mb = 0; mb < C::DBLK; ++mb) dq[mb] = f32x16_t{};
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  for (int t = 0; t < n; ++t) {
-    const int cur = t & 1;
+  // One 32-key tile with its LDS slot fixed at compile time (the loop below alternates the two);
+  // only tiles past the wave's diagonal or the end of the keys are masked element by element.
+  auto tile = [&](int t, auto slot) {
+    constexpr int cur = decltype(slot)::value;
     if (t + 1 < n) issue(t + 1, cur ^ 1);
     const FA_LDS char* kt = (const FA_LDS char*)kb[cur];
     const FA_LDS char* vt = (const FA_LDS char*)vb[cur];
@@ -173,22 +172,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // P^T and dS^T; register j of lane-half hh holds key 16 (j / 8) + 8 hh + j % 8 of the tile
     const int tile0 = t * C::BC;
     const bool need_mask = (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag);
-    const int lim = CAUSAL ? min(Nk - 1, q + diag) : Nk - 1;
     u32x4_t dsb[2];
+    auto ds_tile = [&](auto mask_tag) {
+      const int lim = CAUSAL ? min(Nk - 1, q + diag) : Nk - 1;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float v2[2];
+        for (int u = 0; u < 4; ++u) {
+          float v2[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = 8 * t2 + 2 * u + e;
-          float p = fast_exp2(__builtin_fmaf(s[j], sl2, -l2));
-          if (need_mask && tile0 + 16 * t2 + 8 * hh + 2 * u + e > lim) p = 0.f;
-          v2[e] = p * (dp[j] - dr);
+          for (int e = 0; e < 2; ++e) {
+            const int j = 8 * t2 + 2 * u + e;
+            float p = fast_exp2(__builtin_fmaf(s[j], sl2, -l2));
+            if constexpr (decltype(mask_tag)::value) {
+              if (tile0 + 16 * t2 + 8 * hh + 2 * u + e > lim) p = 0.f;
+            }
+            v2[e] = p * (dp[j] - dr);
+          }
+          dsb[t2][u] = pack_bf16x2(v2[0], v2[1]);
         }
-        dsb[t2][u] = pack_bf16x2(v2[0], v2[1]);
-      }
+    };
+    if (need_mask)
+      ds_tile(std::true_type{});
+    else
+      ds_tile(std::false_type{});
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
@@ -201,7 +208,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
     __syncthreads();                     // ... for every wave, and this tile's reads are done
+  };
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  int t = 0;
+  for (; t + 1 < n; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    tile(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < n) tile(t, std::integral_constant<int, 0>{});
 
   if (q < Nq) {
     uint16_t* op = dQ + ((int64_t)bh * Nq + q) * D + 4 * hh;
