@@ -31,6 +31,14 @@ namespace {
 
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
+// Work item of this workgroup.  Consecutive workgroups go to the eight XCDs in turn; remapping
+// them so that XCD x runs the contiguous item range x * n / 8 .. keeps the items of one head on
+// one XCD, where they share that head's tiles in the XCD's L2.
+__device__ __forceinline__ int xcd_item() {
+  const int g = blockIdx.x, n = gridDim.x;
+  return (n % 8 == 0) ? (g % 8) * (n / 8) + g / 8 : g;
+}
+
 // ------------------------------------------------------------------ preprocess
 // One 16-lane group per query row: Dr = dO . O (fp32 sum of bf16 products), L2 = LSE * log2 e.
 template <int D>
@@ -82,8 +90,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char vb[2][C::TILE_BYTES];
 
   // heaviest query blocks first (causal), each head's blocks together
-  const int qblk = CAUSAL ? n_qblk - 1 - (int)(blockIdx.x % n_qblk) : (int)(blockIdx.x % n_qblk);
-  const int bh = blockIdx.x / n_qblk;
+  const int item = xcd_item();
+  const int qblk = CAUSAL ? n_qblk - 1 - item % n_qblk : item % n_qblk;
+  const int bh = item / n_qblk;
   const int kvh = (bh / H) * (H / group) + (bh % H) / group;
   const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
   const uint16_t* Vh = V + (int64_t)kvh * Nk * D;
@@ -283,8 +292,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char ob[2][C::TILE_BYTES];
   __shared__ __attribute__((aligned(256))) float sb[2][2 * C::BQ];  // [L2 x 32][Dr x 32]
 
-  const int kblk = blockIdx.x % n_kblk;
-  const int bkv = blockIdx.x / n_kblk;  // b * H_kv + kv head
+  const int item = xcd_item();
+  const int kblk = item % n_kblk;
+  const int bkv = item / n_kblk;  // b * H_kv + kv head
   const int H_kv = H / group;
   const int b = bkv / H_kv, hk = bkv % H_kv;
   const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, L = lane & 15;
@@ -365,9 +375,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // One 32-query tile with its LDS slot fixed at compile time (the loop below alternates the
     // two), so every LDS address is a per-lane base plus an immediate.  Only tiles that reach past
     // the wave's diagonal or the end of the queries are masked element by element.
+    // Query tiles are visited from the last one down, so that the workgroups of one head (all on
+    // one XCD) read the same tile at about the same time whatever their first tile.
     auto tile = [&](int t, auto slot) {
       constexpr int cur = decltype(slot)::value;
-      if (t + 1 < n_qt) issue(t + 1, cur ^ 1);
+      if (t - 1 >= q_first) issue(t - 1, cur ^ 1);
       const FA_LDS char* qt = (const FA_LDS char*)qb[cur];
       const FA_LDS char* ot = (const FA_LDS char*)ob[cur];
       const FA_LDS float* st = (const FA_LDS float*)sb[cur];
@@ -435,15 +447,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __syncthreads();
     };
 
-    if (q_first < n_qt) issue(q_first, 0);
+    if (q_first < n_qt) issue(n_qt - 1, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    int t = q_first;
-    for (; t + 1 < n_qt; t += 2) {
+    int t = n_qt - 1;
+    for (; t - 1 >= q_first; t -= 2) {
       tile(t, std::integral_constant<int, 0>{});
-      tile(t + 1, std::integral_constant<int, 1>{});
+      tile(t - 1, std::integral_constant<int, 1>{});
     }
-    if (t < n_qt) tile(t, std::integral_constant<int, 0>{});
+    if (t >= q_first) tile(t, std::integral_constant<int, 0>{});
   }
 
   // dK = scale dK^T^T, dV = dV^T^T: register j of block db is dim 16 db + 4 G + j of key `key`
