@@ -244,6 +244,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ dK, dV
+#ifndef FA_BWD_LOOKAHEAD
+#define FA_BWD_LOOKAHEAD 7  // MFMAs by which the dK/dV kernel's LDS operand reads run ahead
+#endif
+
 template <int D>
 struct DkvCfg {
   static constexpr int WAVES = 8;
@@ -383,19 +387,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const FA_LDS char* qt = (const FA_LDS char*)qb[cur];
       const FA_LDS char* ot = (const FA_LDS char*)ob[cur];
       const FA_LDS float* st = (const FA_LDS float*)sb[cur];
+      // S = Q K^T and dP = dO V^T as an explicit pipeline: MFMA i (k-step i / 4, block (i / 2) % 2,
+      // S for even i, dP for odd) reads its A operand FA_BWD_LOOKAHEAD MFMAs ahead, since a
+      // 16-cycle MFMA cannot cover an LDS read on its own; the four accumulators alternate.
+      constexpr int LA = FA_BWD_LOOKAHEAD;
       f32x4v_t s[2], dp[2];
 #pragma unroll
       for (int bl = 0; bl < 2; ++bl) {
         s[bl] = f32x4v_t{};
         dp[bl] = f32x4v_t{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          s[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lds_load16(qt + roff[bl][ks])), kf[ks], s[bl], 0,
-                                                           0, 0);
-          dp[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lds_load16(ot + roff[bl][ks])), vf[ks], dp[bl],
-                                                            0, 0, 0);
-        }
       }
+      {
+        constexpr int NA = 4 * C::KS;
+        u32x4_t fa[LA + 1];
+        auto read_a = [&](auto I) {
+          constexpr int i = decltype(I)::value;
+          fa[i % (LA + 1)] = lds_load16(((i & 1) ? ot : qt) + roff[(i >> 1) & 1][i >> 2]);
+        };
+        static_for<LA>([&](auto I) { read_a(I); });
+        static_for<NA>([&](auto I) {
+          constexpr int i = decltype(I)::value, bl = (i >> 1) & 1, ks = i >> 2;
+          if constexpr (i & 1)
+            dp[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fa[i % (LA + 1)]), vf[ks], dp[bl], 0, 0, 0);
+          else
+            s[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fa[i % (LA + 1)]), kf[ks], s[bl], 0, 0, 0);
+          if constexpr (i + LA < NA) read_a(std::integral_constant<int, i + LA>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      // the first transposing reads of dV^T / dK^T go out now, under the P and dS arithmetic
+      constexpr int NC = 2 * C::DB;
+      u32x4_t fc[LA + 1];
+      auto read_c = [&](auto I) {  // MFMA i: dV^T block i / 2 (even i, from dO) or dK^T (odd, from Q)
+        constexpr int i = decltype(I)::value, db = i >> 1;
+        const FA_LDS char* base = (i & 1) ? qt : ot;
+        const i16x4_t lo = lds_load8_tr16(base + tr_off(0, db));
+        const i16x4_t hi = lds_load8_tr16(base + tr_off(1, db));
+        fc[i % (LA + 1)] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      static_for<LA>([&](auto I) { read_c(I); });
+      __builtin_amdgcn_sched_barrier(0);
       // P and dS for queries q0 + 8 G + 4 bl + j against this lane's key
       const int q0 = t * C::BQ;
       const f32x4v_t l2a = *(const FA_LDS f32x4v_t*)(st + 8 * G);
@@ -431,18 +462,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         p_ds(std::true_type{});
       else
         p_ds(std::false_type{});
-      // dV^T += dO^T P,  dK^T += Q^T dS  (k = the tile's 32 queries)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const i16x4_t olo = lds_load8_tr16(ot + tr_off(0, db));
-        const i16x4_t ohi = lds_load8_tr16(ot + tr_off(1, db));
-        const bf16x8_t ao = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
-        dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, as_bf16x8(pB), dv[db], 0, 0, 0);
-        const i16x4_t qlo = lds_load8_tr16(qt + tr_off(0, db));
-        const i16x4_t qhi = lds_load8_tr16(qt + tr_off(1, db));
-        const bf16x8_t aq = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-        dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, as_bf16x8(dsB), dk[db], 0, 0, 0);
-      }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (k = the tile's 32 queries), reads LA MFMAs ahead
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<NC>([&](auto I) {
+        constexpr int i = decltype(I)::value, db = i >> 1;
+        if constexpr (i & 1)
+          dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fc[i % (LA + 1)]), as_bf16x8(dsB), dk[db], 0, 0, 0);
+        else
+          dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fc[i % (LA + 1)]), as_bf16x8(pB), dv[db], 0, 0, 0);
+        if constexpr (i + LA < NC) read_c(std::integral_constant<int, i + LA>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
     };
