@@ -130,23 +130,25 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   // ---- asynchronous global -> LDS tile loads, issued by the four waves of group 0 inside their
   // MFMA phases (their vector units are idle there).  One instruction moves 16 bytes per lane
   // into 1 KiB of consecutive LDS; lane L lands in row L / CPR, slot L % CPR of its rows, so it
-  // fetches the global chunk that the row's swizzle puts in that slot.  Addresses are a buffer
-  // resource over the head's K or V plus a 32-bit per-lane byte offset; rows past the end of the
-  // keys are clamped to the last key (their scores are masked).
+  // fetches the global chunk that the row's swizzle puts in that slot.  Each tile gets its own
+  // buffer resource, starting at the tile's first key and ending at the last key of the head, so
+  // the per-lane byte offset is the same for every tile and a load costs no vector instruction.
+  // Rows past the last key fall outside the resource: the hardware range check returns zeros
+  // for them without touching memory (their scores are masked; the LDS rings are zero-filled at
+  // kernel start, so those rows hold finite values in any case).
   const int lw = wave & 3;
-  int dma_row[C::DMA_PER_WAVE], dma_cb[C::DMA_PER_WAVE];
+  int dma_off[C::DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
     const int row = (lw * C::DMA_PER_WAVE + i) * C::ROWS_PER_DMA + lane / C::CPR;
-    dma_row[i] = row;
-    dma_cb[i] = ((lane % C::CPR) ^ swz<D>(row)) * 16;
+    dma_off[i] = row * C::RB + ((lane % C::CPR) ^ swz<D>(row)) * 16;
   }
-  const __amdgpu_buffer_rsrc_t Kr = raw_rsrc(Kh, Nk * C::RB), Vr = raw_rsrc(Vh, Nk * C::RB);
-  auto issue_one = [&](__amdgpu_buffer_rsrc_t src, int t, char* buf, int i) {
-    const uint32_t off = (uint32_t)min(tile_of(t) * C::BC + dma_row[i], Nk - 1) * C::RB + dma_cb[i];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, off, 0, 0, 0);
+  auto issue_one = [&](const uint16_t* src, int t, char* buf, int i) {
+    const int r0 = tile_of(t) * C::BC;
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(src + (int64_t)r0 * D, (Nk - r0) * C::RB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, dma_off[i], 0, 0, 0);
   };
-  auto issue = [&](__amdgpu_buffer_rsrc_t src, int t, char* buf) {
+  auto issue = [&](const uint16_t* src, int t, char* buf) {
 #pragma unroll
     for (int i = 0; i < C::DMA_PER_WAVE; ++i) issue_one(src, t, buf, i);
   };
@@ -216,7 +218,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   // NS + NP slots.  Slot i issues MFMA i (S MFMAs first, then the PV MFMAs), then the LDS reads of
   // the A operand of MFMA i + L into a rotating set of L + 1 fragment registers, and, when this
   // wave moves tiles, every DMA_EVERY-th slot one of its global -> LDS loads of K_{j+1} (a
-  // harmless clamped reload when j + 1 = n) and V_j into the free slots kdst and vdst.  Scheduling
+  // harmless reload of a valid tile when j + 1 = n) and V_j into the free slots kdst and vdst.  Scheduling
   // barriers between slots keep the compiler from collapsing the read-ahead.
   auto mfma_phase = [&](auto load_tag, int j, const char* kbuf, const char* vbuf, char* kdst, char* vdst) {
     constexpr int NS = 2 * C::KSTEPS, NP = 4 * C::DBLK, N = NS + NP, L = FA_LOOKAHEAD;
@@ -254,9 +256,9 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
       if constexpr (NDMA > 0 && i % DMA_EVERY == 0 && i / DMA_EVERY < NDMA) {
         constexpr int d = i / DMA_EVERY;
         if constexpr (d < C::DMA_PER_WAVE)
-          issue_one(Kr, j + 1, kdst, d);
+          issue_one(Kh, j + 1, kdst, d);
         else
-          issue_one(Vr, j, vdst, d - C::DMA_PER_WAVE);
+          issue_one(Vh, j, vdst, d - C::DMA_PER_WAVE);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -283,7 +285,10 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
 #pragma unroll
     for (int jj = 2; jj < 15; ++jj) mx = max3f(mx, s1[jj], s0[jj + 1]);
     mx = max3f(mx, s1[15], s1[15]);
-    mx = max_across_halves(mx) * sl2;
+    {  // across the two lane halves, without fmaxf's canonicalising of the swapped values
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1])) * sl2;
+    }
     if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
       const float mnew = fmaxf(m2, mx);
       const float alpha = fast_exp2(m2 - mnew);
@@ -293,7 +298,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
       for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] *= alpha;
     }
     const float nm = -m2;
-    float rs = 0.f;
+    float rs;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const f32x16_t& s = (t < 2) ? s0 : s1;
@@ -302,7 +307,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
       for (int u = 0; u < 4; ++u) {
         const float pa = fast_exp2(__builtin_fmaf(s[j0 + 2 * u], sl2, nm));
         const float pc = fast_exp2(__builtin_fmaf(s[j0 + 2 * u + 1], sl2, nm));
-        rs += pa + pc;
+        rs = (t == 0 && u == 0) ? pa + pc : rs + (pa + pc);
         pb[t][u] = pack_bf16x2(pa, pc);
       }
     }
@@ -324,13 +329,13 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   constexpr std::integral_constant<bool, true> LOAD{};
   constexpr std::integral_constant<bool, false> NOLOAD{};
 
-  if (group == 0) issue(Kr, 0, kb0);
+  if (group == 0) issue(Kh, 0, kb0);
   wait_loads();
   bar();
   // Slots by tile parity: K_j in kb[j & 1], V_j in vb[j & 1].  Every wave runs 2n + 3 barriers.
   if (group == 0) {
-    issue(Kr, 1, kb1);  // h = 0 (K_1 is a clamped reload of K_0 when n = 1)
-    issue(Vr, 0, vb0);
+    issue(Kh, 1, kb1);  // h = 0 (K_1 is a harmless reload of K_0 when n = 1)
+    issue(Vh, 0, vb0);
     qk(kb0);
     fence_acc();
     bar();
@@ -433,6 +438,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char vb0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb1[C::TILE_BYTES];
 
+  // Zero-fill the rings once, so that no K/V row a masked score meets ever holds a non-finite
+  // bit pattern (0 * inf would poison O).
+  {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = threadIdx.x * 16; i < C::TILE_BYTES; i += C::THREADS * 16) {
+      lds_store16((FA_LDS char*)(kb0 + i), z);
+      lds_store16((FA_LDS char*)(kb1 + i), z);
+      lds_store16((FA_LDS char*)(vb0 + i), z);
+      lds_store16((FA_LDS char*)(vb1 + i), z);
+    }
+    __syncthreads();
+  }
   const int g = blockIdx.x;
   int it = g, it_end = n_items, stride = gridDim.x;
   if (xcd_split) {
