@@ -129,21 +129,24 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
     return x >= n ? x - n : x;
   };
 
-  // ---- global -> LDS tile loads (group 0, inside its MFMA phases); LDS row = key row of the tile
+  // ---- global -> LDS tile loads (group 0, inside its MFMA phases); LDS row = key row of the tile.
+  // Each tile gets its own buffer resource (base at the tile's first key, range ending at the
+  // head's last key), so a lane's byte offset is the same for every tile and a load costs no
+  // vector instruction; rows past the last key are outside the range and read as zero without a
+  // memory access (the rings are zero-filled at kernel start as well).
   const int lw = wave & 3;
-  int dma_row[C::DMA_PER_WAVE], dma_cb[C::DMA_PER_WAVE];
+  int dma_off[C::DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
     const int row = (lw * C::DMA_PER_WAVE + i) * C::ROWS_PER_DMA + lane / C::CPR;
-    dma_row[i] = row;
-    dma_cb[i] = ((lane % C::CPR) ^ swz8<D>(row)) * 16;
+    dma_off[i] = row * C::RB + ((lane % C::CPR) ^ swz8<D>(row)) * 16;
   }
-  const __amdgpu_buffer_rsrc_t Kr = raw_rsrc(Kh, Nk * C::RB), Vr = raw_rsrc(Vh, Nk * C::RB);
-  auto issue_one = [&](__amdgpu_buffer_rsrc_t src, int t, char* buf, int i) {
-    const uint32_t off = (uint32_t)min(tile_of(t) * C::BC + dma_row[i], Nk - 1) * C::RB + dma_cb[i];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, off, 0, 0, 0);
+  auto issue_one = [&](const uint8_t* src, int t, char* buf, int i) {
+    const int r0 = tile_of(t) * C::BC;
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(src + (int64_t)r0 * C::RB, (Nk - r0) * C::RB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, dma_off[i], 0, 0, 0);
   };
-  auto issue = [&](__amdgpu_buffer_rsrc_t src, int t, char* buf) {
+  auto issue = [&](const uint8_t* src, int t, char* buf) {
 #pragma unroll
     for (int i = 0; i < C::DMA_PER_WAVE; ++i) issue_one(src, t, buf, i);
   };
@@ -235,9 +238,9 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
       if constexpr (NDMA > 0 && i % DMA_EVERY == 0 && i / DMA_EVERY < NDMA) {
         constexpr int d = i / DMA_EVERY;
         if constexpr (d < C::DMA_PER_WAVE)
-          issue_one(Kr, j + 1, kdst, d);
+          issue_one(Kh, j + 1, kdst, d);
         else
-          issue_one(Vr, j, vdst, d - C::DMA_PER_WAVE);
+          issue_one(Vh, j, vdst, d - C::DMA_PER_WAVE);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -298,12 +301,12 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
   constexpr std::integral_constant<bool, true> LOAD{};
   constexpr std::integral_constant<bool, false> NOLOAD{};
 
-  if (group == 0) issue(Kr, 0, kb0);
+  if (group == 0) issue(Kh, 0, kb0);
   wait_loads();
   bar();
   if (group == 0) {
-    issue(Kr, 1, kb1);
-    issue(Vr, 0, vb0);
+    issue(Kh, 1, kb1);
+    issue(Vh, 0, vb0);
     qk(kb0);
     fence_acc();
     bar();
@@ -397,6 +400,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char vb0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb1[C::TILE_BYTES];
 
+  // Zero-fill the rings once, so that no K/V row a masked score meets ever holds a non-finite value.
+  {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = threadIdx.x * 16; i < C::TILE_BYTES; i += C::THREADS * 16) {
+      lds_store16((FA_LDS char*)(kb0 + i), z);
+      lds_store16((FA_LDS char*)(kb1 + i), z);
+      lds_store16((FA_LDS char*)(vb0 + i), z);
+      lds_store16((FA_LDS char*)(vb1 + i), z);
+    }
+    __syncthreads();
+  }
   const int g = blockIdx.x;
   int it = g, it_end = n_items, stride = gridDim.x;
   if (xcd_split) {
