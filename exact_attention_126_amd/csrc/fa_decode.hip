@@ -22,6 +22,12 @@
 namespace fa {
 namespace {
 
+// 16-byte load of K/V cache data that is read exactly once: the non-temporal hint keeps the stream
+// from displacing reusable lines (the split partials the combine reads next) in the caches.
+__device__ __forceinline__ u32x4_t stream_load16(const void* p) {
+  return __builtin_nontemporal_load((const u32x4_t*)p);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
   constexpr int EPL = Elt<T>::PER16;  // elements per lane per key row
   constexpr int LPK = D / EPL;        // lanes per key row
   constexpr int KPW = 64 / LPK;       // key rows per wave per step
-  constexpr int U = 8;                // steps in flight per iteration (the same for every GE)
+  constexpr int U = 16;               // steps in flight per iteration (the same for every GE)
   constexpr int WAVES = 4;
   __shared__ float s_m[WAVES][GE], s_l[WAVES][GE];
   __shared__ float s_acc[WAVES][GE][D];
@@ -111,8 +117,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = min(base + u * KPW + gi, end - 1);
-      kr[u] = gload16(Kh + (int64_t)key * D);
-      vr[u] = gload16(Vh + (int64_t)key * D);
+      kr[u] = stream_load16(Kh + (int64_t)key * D);
+      vr[u] = stream_load16(Vh + (int64_t)key * D);
     }
     float sc[U][GE];
     float bm[GE];
@@ -268,8 +274,8 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(const uint16_t* _
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = min(base + u * KPW + gi, end - 1);
-      kr[u] = gload16(Kh + (int64_t)key * D);
-      vr[u] = gload16(Vh + (int64_t)key * D);
+      kr[u] = stream_load16(Kh + (int64_t)key * D);
+      vr[u] = stream_load16(Vh + (int64_t)key * D);
     }
     float sc[U][GE];
     float bm[GE];
