@@ -31,7 +31,7 @@ def hipcc() -> str:
 def flags(save_temps: bool = False):
     f = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
+         "-Wall", "-Wno-unused-result", "-Wl,--no-undefined", "-I", INCLUDE, "-I", CSRC]
     if save_temps:
         f.append("--save-temps")
     return f
