@@ -238,6 +238,23 @@ def time_extras(torch, fa, si, get, reps: int = 20) -> dict:
         return e0.elapsed_time(e1) / n
 
     out = {}
+    # the other forward workloads: the tiny fp32 case, the short d = 64 batch and the long context
+    for name in ("tiny_f32_n128_d64", "batch_b4h16_n2048_d64", "long_b1h32_n16384_d128_causal"):
+        w = get(name)
+        if w.dtype == "f32":
+            dev = {x: torch.from_numpy(si.make_tensor(w, x)).cuda() for x in "qkv"}
+        else:
+            dev = {x: to_device(w, si.make_tensor(w, x)) for x in "qkv"}
+        o = torch.empty_like(dev["q"])
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+        n = 10 * reps if w.dtype == "f32" else reps
+        ms = timed(lambda: fa.fa_fwd(dev["q"], dev["k"], dev["v"], o, lse, causal=w.causal, scale=w.scale,
+                                     stream=stream), n, n)
+        tf = 4.0 * w.B * w.H * w.Nq * w.Nk * w.d / (2 if w.causal else 1) / (ms * 1e-3) / 1e12
+        out[name] = {"workload": w.name, "entry": "fa_fwd (" + ("fp32" if w.dtype == "f32" else "bf16") +
+                     (", causal)" if w.causal else ")"), "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+                     "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+        del dev, o, lse
     w = get("chunk_prefill_b1h32kv8_nq2048_nk16384_d128")
     dev = {x: to_device(w, si.make_tensor(w, x)) for x in "qkv"}
     o = torch.empty_like(dev["q"])
