@@ -369,9 +369,11 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
   const int dim = threadIdx.x;
   const float* ml = ML + (int64_t)bh * S * 2;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
   float L = 0.f, acc = 0.f;
   const float* op = Opart + (int64_t)bh * S * D + dim;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) {
     const float f = fast_exp2((ml[2 * s] - M) * kLog2e);  // empty split: exp2(-inf) = 0
     L = __builtin_fmaf(f, ml[2 * s + 1], L);
