@@ -42,6 +42,10 @@
 //    nothing); uniform work keeps the two groups in lockstep.  Query blocks with the most
 //    tiles are dispatched first, and workgroups are remapped so that the ones an XCD runs
 //    together share a head's K/V in that XCD's L2.
+//  * The output leaves through LDS: each wave's 32 x D output block is contiguous in HBM, so it is
+//    transposed in a per-wave staging area and written with 16-byte stores covering whole rows
+//    (stored straight from the accumulator layout, every store instruction touched 32 rows and
+//    the next block's first wait sat behind them).
 //  * exp is the hardware exp2 with scale * log2(e) folded into one FMA; LSE is emitted in
 //    natural-log units.
 #include "fa_device.h"
@@ -93,7 +97,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
                                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                           float* __restrict__ LSE, int Nq, int Nk, float sl2, int bh, int kvh,
                                           int diag, int qblk, int n_qblk, char* kb0, char* kb1, char* vb0,
-                                          char* vb1) {
+                                          char* vb1, char* stg) {
   using C = Bf16Cfg<D>;
   const uint16_t* Qh = Q + (int64_t)bh * Nq * D;
   const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
@@ -395,25 +399,41 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
     bar();
   }
 
-  // ---- epilogue: O = O_acc / l (RNE to bf16), LSE = (m + log2 l) * ln 2
+  // ---- epilogue: O = O_acc / l (RNE to bf16), LSE = (m + log2 l) * ln 2.  The wave's 32 output
+  // rows are one contiguous 32 x D block of O; a lane holds 8-byte pieces of one row, so the block
+  // is first transposed through the wave's own LDS staging area (16-byte chunks XOR-swizzled by
+  // the row) and then written with 16-byte stores that each cover whole rows.
   uint16_t* Oh = O + (int64_t)bh * Nq * D;
   float* Lh = LSE + (int64_t)bh * Nq;
   const float l = sum_across_halves(lsum);
   const float inv = 1.f / l;
   const int q = q_wave0 + l32;
-  if (q < Nq) {
-    uint16_t* op = Oh + (int64_t)q * D + 4 * hh;
+  // Lane index behind an empty asm: the staging addresses below are derived from it, so the
+  // compiler cannot hoist them into the tile loop, where they would hold registers for nothing.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int r32 = ln & 31, h2 = ln >> 5;
+  FA_LDS char* st = (FA_LDS char*)(stg + wave * 32 * C::RB);
 #pragma unroll
-    for (int mb = 0; mb < C::DBLK; ++mb)
+  for (int mb = 0; mb < C::DBLK; ++mb)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        u32x2_t w;
-        w[0] = pack_bf16x2(oacc[mb][4 * jg + 0] * inv, oacc[mb][4 * jg + 1] * inv);
-        w[1] = pack_bf16x2(oacc[mb][4 * jg + 2] * inv, oacc[mb][4 * jg + 3] * inv);
-        *(u32x2_t*)(op + 32 * mb + 8 * jg) = w;
-      }
-    if (hh == 0) Lh[q] = (m2 + fast_log2(l)) * kLn2;
+    for (int jg = 0; jg < 4; ++jg) {
+      u32x2_t w;
+      w[0] = pack_bf16x2(oacc[mb][4 * jg + 0] * inv, oacc[mb][4 * jg + 1] * inv);
+      w[1] = pack_bf16x2(oacc[mb][4 * jg + 2] * inv, oacc[mb][4 * jg + 3] * inv);
+      const int chunk = 4 * mb + jg;
+      *(FA_LDS u32x2_t*)(st + r32 * C::RB + ((chunk ^ (r32 % C::CPR)) << 4) + 8 * h2) = w;
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 32 * C::RB / 1024; ++i) {
+    const int flat = i * 1024 + ln * 16;
+    const int row = flat / C::RB, chunk = (flat % C::RB) >> 4;
+    const u32x4_t v = lds_load16(st + row * C::RB + ((chunk ^ (row % C::CPR)) << 4));
+    if (q_wave0 + row < Nq) *(u32x4_t*)(Oh + (int64_t)(q_wave0 + row) * D + chunk * 8) = v;
   }
+  if (q < Nq && hh == 0) Lh[q] = (m2 + fast_log2(l)) * kLn2;
 }
 
 // Persistent kernel: one workgroup per CU loops over work items.  A causal item is the pair of
@@ -437,6 +457,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char kb1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb1[C::TILE_BYTES];
+  // Per-wave staging of the output block (epilogue only).  Its smaller alignment places it after
+  // the rings, whose LDS offsets must stay below 64 KiB to fit the immediate offset of ds_read
+  // (placed first, it pushed every ring address past that limit and cost an address add per read).
+  __shared__ __attribute__((aligned(16))) char stg[C::WAVES * 32 * C::RB];
 
   // Zero-fill the rings once, so that no K/V row a masked score meets ever holds a non-finite
   // bit pattern (0 * inf would poison O).
@@ -466,7 +490,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int cnt = (CAUSAL && paired && r != qa) ? 2 : 1;
     for (int k = 0; k < cnt; ++k)
       fwd_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, k == 0 ? qa : r, n_qblk, kb0, kb1, vb0,
-                           vb1);
+                           vb1, stg);
   }
 }
 
