@@ -70,6 +70,9 @@ struct Bf16Cfg {
   static constexpr int KSTEPS = D / 16;                             // MFMA k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 32;                               // 32-dim blocks of O^T
   static_assert(TILE_BYTES % (1024 * LOADERS) == 0, "tile must split evenly into wave loads");
+  struct QFrag {
+    bf16x8_t f[KSTEPS];
+  };
 };
 
 // Lazy rescaling threshold, log2 units: the running max used for the exponentials is only
@@ -93,11 +96,12 @@ constexpr float kLazyRescale = 8.f;
 // with the LDS rings kb0/kb1 (K) and vb0/vb1 (V).  The first barrier it executes orders its LDS
 // use after the previous block's; its last barrier is passed only when every wave is done.
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                           float* __restrict__ LSE, int Nq, int Nk, float sl2, int bh, int kvh,
                                           int diag, int qblk, int n_qblk, char* kb0, char* kb1, char* vb0,
-                                          char* vb1, char* stg) {
+                                          char* vb1, char* stg, bf16x8_t (&qf)[Bf16Cfg<D>::KSTEPS], bool pre,
+                                          bool has_next, int nbh, int nkvh, int nqblk) {
   using C = Bf16Cfg<D>;
   const uint16_t* Qh = Q + (int64_t)bh * Nq * D;
   const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
@@ -109,14 +113,14 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   const int group = wave >> 2;
   const int q_wave0 = qblk * C::BR + wave * 32;  // first query of this wave (wave-uniform)
 
-  // ---- Q^T fragments (B operand), resident for the whole kernel
-  bf16x8_t qf[C::KSTEPS];
-  {
-    const int qrow = min(q_wave0 + l32, Nq - 1);
-    const uint16_t* qp = Qh + (int64_t)qrow * D + 8 * hh;
+  // ---- Q^T fragments (B operand), resident for the block (loaded by the previous block when pre)
+  auto load_q = [&](const uint16_t* qhead, int qw0) {
+    const int qrow = min(qw0 + l32, Nq - 1);
+    const uint16_t* qp = qhead + (int64_t)qrow * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = as_bf16x8(gload16(qp + 16 * ks));
-  }
+  };
+  if (!pre) load_q(Qh, q_wave0);
 
   // ---- the workgroup streams n tiles and every wave processes all of them.  Without a mask the
   // tile order is free, so query blocks of one head start at different tiles (rotation rot):
@@ -147,9 +151,16 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
     const int row = (lw * C::DMA_PER_WAVE + i) * C::ROWS_PER_DMA + lane / C::CPR;
     dma_off[i] = row * C::RB + ((lane % C::CPR) ^ swz<D>(row)) * 16;
   }
+  // With an even tile count the step past the last tile reloads into kb0; when a next block
+  // follows, that load fetches the next block's first K tile instead (it lands in kb0, where the
+  // next block expects it), and the next block's Q is loaded during this block's last phase.
+  const bool do_pf = has_next && (n % 2 == 0);
+  const uint16_t* nKh = K + (int64_t)nkvh * Nk * D;
+  const int nrot = CAUSAL ? 0 : (int)(((int64_t)nqblk * n) / n_qblk);
   auto issue_one = [&](const uint16_t* src, int t, char* buf, int i) {
-    const int r0 = tile_of(t) * C::BC;
-    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(src + (int64_t)r0 * D, (Nk - r0) * C::RB);
+    const bool nxt = do_pf && t >= n;
+    const int r0 = (nxt ? nrot : tile_of(t)) * C::BC;
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc((nxt ? nKh : src) + (int64_t)r0 * D, (Nk - r0) * C::RB);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(buf + (lw * C::DMA_PER_WAVE + i) * 1024), 16, dma_off[i], 0, 0, 0);
   };
   auto issue = [&](const uint16_t* src, int t, char* buf) {
@@ -333,9 +344,11 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
   constexpr std::integral_constant<bool, true> LOAD{};
   constexpr std::integral_constant<bool, false> NOLOAD{};
 
-  if (group == 0) issue(Kh, 0, kb0);
-  wait_loads();
-  bar();
+  if (!pre) {
+    if (group == 0) issue(Kh, 0, kb0);
+    wait_loads();
+    bar();
+  }
   // Slots by tile parity: K_j in kb[j & 1], V_j in vb[j & 1].  Every wave runs 2n + 3 barriers.
   if (group == 0) {
     issue(Kh, 1, kb1);  // h = 0 (K_1 is a harmless reload of K_0 when n = 1)
@@ -367,6 +380,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
     softmax_phase(n - 1);  // h = 2n - 1
     wait_loads();
     bar();
+    if (do_pf) load_q(Q + (int64_t)nbh * Nq * D, nqblk * C::BR + wave * 32);
     pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n
     bar();
     bar();  // h = 2n + 1: group 1 finishes
@@ -395,6 +409,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
     }
     softmax_phase(n - 1);  // h = 2n
     bar();
+    if (do_pf) load_q(Q + (int64_t)nbh * Nq * D, nqblk * C::BR + wave * 32);
     pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n + 1
     bar();
   }
@@ -434,6 +449,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* __restrict__ Q, const 
     if (q_wave0 + row < Nq) *(u32x4_t*)(Oh + (int64_t)(q_wave0 + row) * D + chunk * 8) = v;
   }
   if (q < Nq && hh == 0) Lh[q] = (m2 + fast_log2(l)) * kLn2;
+  return do_pf;
 }
 
 // Persistent kernel: one workgroup per CU loops over work items.  A causal item is the pair of
@@ -483,14 +499,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     it_end = (g & 7) * per + per;
     stride = gridDim.x >> 3;
   }
-  for (; it < it_end; it += stride) {
-    const int bh = it / items_per_head, r = it % items_per_head;
-    const int kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
+  // Block k of item it: its head, K/V head and query block, and the number of blocks of the item.
+  auto block_of = [&](int item, int k, int& bh, int& kvh, int& qblk) {
+    bh = item / items_per_head;
+    const int r = item % items_per_head;
+    kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
     const int qa = CAUSAL ? n_qblk - 1 - r : r;
-    const int cnt = (CAUSAL && paired && r != qa) ? 2 : 1;
-    for (int k = 0; k < cnt; ++k)
-      fwd_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, k == 0 ? qa : r, n_qblk, kb0, kb1, vb0,
-                           vb1, stg);
+    qblk = k == 0 ? qa : r;
+    return (CAUSAL && paired && r != qa) ? 2 : 1;
+  };
+  typename Bf16Cfg<D>::QFrag qf;
+  bool pre = false;
+  int k = 0;
+  while (it < it_end) {
+    int bh, kvh, qblk;
+    const int cnt = block_of(it, k, bh, kvh, qblk);
+    int it2 = it, k2 = k + 1;
+    if (k2 >= cnt) {
+      it2 += stride;
+      k2 = 0;
+    }
+    const bool has_next = it2 < it_end;
+    int nbh = bh, nkvh = kvh, nqblk = qblk;
+    if (has_next) block_of(it2, k2, nbh, nkvh, nqblk);
+    pre = fwd_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, qblk, n_qblk, kb0, kb1, vb0, vb1, stg,
+                               qf.f, pre, has_next, nbh, nkvh, nqblk);
+    it = it2;
+    k = k2;
   }
 }
 
