@@ -85,6 +85,17 @@ constexpr float kLazyRescale = 8.f;
 #define FA_LOOKAHEAD 8  // MFMAs by which LDS operand reads run ahead
 #endif
 
+// Q^T fragments (the B operand of S^T = K Q^T) of the 32 queries from qw0 of query head bh:
+// lane (l32, hh) holds dims 16 ks + 8 hh .. + 7 of query qw0 + l32 (clamped to the last query).
+template <int D>
+__device__ __forceinline__ void load_q_frags(bf16x8_t (&qf)[Bf16Cfg<D>::KSTEPS], const uint16_t* __restrict__ Q,
+                                             int bh, int Nq, int qw0, int l32, int hh) {
+  const int qrow = min(qw0 + l32, Nq - 1);
+  const uint16_t* qp = Q + ((int64_t)bh * Nq + qrow) * D + 8 * hh;
+#pragma unroll
+  for (int ks = 0; ks < Bf16Cfg<D>::KSTEPS; ++ks) qf[ks] = as_bf16x8(gload16(qp + 16 * ks));
+}
+
 // Eight waves: group 0 (waves 0-3) and group 1 (waves 4-7) each cover the four SIMDs, so every
 // SIMD runs one wave of each group.  Time is cut into half-periods separated by workgroup
 // barriers.  In half-period h a wave of group g works on phase p = h - g:
@@ -113,14 +124,10 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   const int group = wave >> 2;
   const int q_wave0 = qblk * C::BR + wave * 32;  // first query of this wave (wave-uniform)
 
-  // ---- Q^T fragments (B operand), resident for the block (loaded by the previous block when pre)
-  auto load_q = [&](const uint16_t* qhead, int qw0) {
-    const int qrow = min(qw0 + l32, Nq - 1);
-    const uint16_t* qp = qhead + (int64_t)qrow * D + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = as_bf16x8(gload16(qp + 16 * ks));
-  };
-  if (!pre) load_q(Qh, q_wave0);
+  // ---- Q^T fragments (B operand) of this block are already in qf: the previous block (or the
+  // kernel, for the first one) loaded them.  This block loads the next block's once its own last
+  // S product is issued.
+  (void)Qh;
 
   // ---- the workgroup streams n tiles and every wave processes all of them.  Without a mask the
   // tile order is free, so query blocks of one head start at different tiles (rotation rot):
@@ -341,6 +348,9 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     asm volatile("" ::: "memory");
   };
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  // vmcnt(KSTEPS): every tile load is done; the next block's Q loads, issued after them, may not be
+  static_assert(C::KSTEPS < 16, "vmcnt field");
+  auto wait_loads_but_q = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70 | C::KSTEPS); };
   constexpr std::integral_constant<bool, true> LOAD{};
   constexpr std::integral_constant<bool, false> NOLOAD{};
 
@@ -377,10 +387,10 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
       bar();
       ++j;
     }
+    load_q_frags<D>(qf, Q, nbh, Nq, nqblk * C::BR + wave * 32, l32, hh);
     softmax_phase(n - 1);  // h = 2n - 1
-    wait_loads();
+    wait_loads_but_q();
     bar();
-    if (do_pf) load_q(Q + (int64_t)nbh * Nq * D, nqblk * C::BR + wave * 32);
     pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n
     bar();
     bar();  // h = 2n + 1: group 1 finishes
@@ -407,9 +417,9 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
       bar();
       ++j;
     }
+    load_q_frags<D>(qf, Q, nbh, Nq, nqblk * C::BR + wave * 32, l32, hh);
     softmax_phase(n - 1);  // h = 2n
     bar();
-    if (do_pf) load_q(Q + (int64_t)nbh * Nq * D, nqblk * C::BR + wave * 32);
     pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n + 1
     bar();
   }
@@ -439,7 +449,9 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
       const int chunk = 4 * mb + jg;
       *(FA_LDS u32x2_t*)(st + r32 * C::RB + ((chunk ^ (r32 % C::CPR)) << 4) + 8 * h2) = w;
     }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+  // lgkmcnt(0): this wave's staging writes are done; vmcnt(0): the next block's Q fragments have
+  // landed (issued two phases ago), so no wait for them lands behind the stores below
+  __builtin_amdgcn_s_waitcnt(0x0070);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int i = 0; i < 32 * C::RB / 1024; ++i) {
@@ -511,6 +523,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   typename Bf16Cfg<D>::QFrag qf;
   bool pre = false;
   int k = 0;
+  if (it < it_end) {
+    int bh, kvh, qblk;
+    block_of(it, 0, bh, kvh, qblk);
+    load_q_frags<D>(qf.f, Q, bh, Nq, qblk * Bf16Cfg<D>::BR + (threadIdx.x >> 6) * 32, threadIdx.x & 31,
+                    (threadIdx.x >> 5) & 1);
+  }
   while (it < it_end) {
     int bh, kvh, qblk;
     const int cnt = block_of(it, k, bh, kvh, qblk);
