@@ -100,7 +100,7 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
                                           const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
                                           float* __restrict__ LSE, int Nq, int Nk, float sl2, float vsc, int bh,
                                           int kvh, int diag, int qblk, int n_qblk, char* kb0, char* kb1, char* vb0,
-                                          char* vb1) {
+                                          char* vb1, char* stg) {
   using C = Fp8Cfg<D>;
   const uint8_t* Qh = Q + (int64_t)bh * Nq * D;
   const uint8_t* Kh = K + (int64_t)kvh * Nk * D;
@@ -372,19 +372,35 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
   const float l = sum_across_halves(lsum);
   const float inv = vsc / l;
   const int q = q_wave0 + l32;
-  if (q < Nq) {
-    uint16_t* op = Oh + (int64_t)q * D + 4 * hh;
+  // The wave's 32 output rows are one contiguous 32 x D bf16 block: transposed through the wave's
+  // LDS staging area (16-byte chunks XOR-swizzled by the row), then stored as whole rows.  The
+  // lane index sits behind an empty asm so that the staging addresses are not hoisted into the
+  // tile loop.
+  constexpr int ORB = D * 2, OCPR = ORB / 16;  // output bytes and 16-byte chunks per row
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int r32 = ln & 31, h2 = ln >> 5;
+  FA_LDS char* st = (FA_LDS char*)(stg + wave * 32 * ORB);
 #pragma unroll
-    for (int mb = 0; mb < C::DBLK; ++mb)
+  for (int mb = 0; mb < C::DBLK; ++mb)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        u32x2_t w;
-        w[0] = pack_bf16x2(oacc[mb][4 * jg + 0] * inv, oacc[mb][4 * jg + 1] * inv);
-        w[1] = pack_bf16x2(oacc[mb][4 * jg + 2] * inv, oacc[mb][4 * jg + 3] * inv);
-        *(u32x2_t*)(op + 32 * mb + 8 * jg) = w;
-      }
-    if (hh == 0) Lh[q] = (m2 - kBias + fast_log2(l)) * kLn2;
+    for (int jg = 0; jg < 4; ++jg) {
+      u32x2_t w;
+      w[0] = pack_bf16x2(oacc[mb][4 * jg + 0] * inv, oacc[mb][4 * jg + 1] * inv);
+      w[1] = pack_bf16x2(oacc[mb][4 * jg + 2] * inv, oacc[mb][4 * jg + 3] * inv);
+      const int chunk = 4 * mb + jg;
+      *(FA_LDS u32x2_t*)(st + r32 * ORB + ((chunk ^ (r32 % OCPR)) << 4) + 8 * h2) = w;
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 32 * ORB / 1024; ++i) {
+    const int flat = i * 1024 + ln * 16;
+    const int row = flat / ORB, chunk = (flat % ORB) >> 4;
+    const u32x4_t v = lds_load16(st + row * ORB + ((chunk ^ (row % OCPR)) << 4));
+    if (q_wave0 + row < Nq) *(u32x4_t*)(Oh + (int64_t)(q_wave0 + row) * D + chunk * 8) = v;
   }
+  if (q < Nq && hh == 0) Lh[q] = (m2 - kBias + fast_log2(l)) * kLn2;
 }
 
 // Persistent kernel with the work items of fwd_bf16_kernel (paired causal blocks, XCD ranges).
@@ -399,6 +415,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char kb1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb1[C::TILE_BYTES];
+  // Per-wave staging of the bf16 output block (epilogue only); its smaller alignment places it
+  // after the rings, whose LDS offsets then stay within the ds_read immediate range.
+  __shared__ __attribute__((aligned(16))) char stg[C::WAVES * 32 * D * 2];
 
   // Zero-fill the rings once, so that no K/V row a masked score meets ever holds a non-finite value.
   {
@@ -429,7 +448,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int cnt = (CAUSAL && paired && r != qa) ? 2 : 1;
     for (int k = 0; k < cnt; ++k)
       fp8_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2h, vsc, bh, kvh, diag, k == 0 ? qa : r, n_qblk, kb0, kb1, vb0,
-                           vb1);
+                           vb1, stg);
   }
 }
 
