@@ -8,7 +8,7 @@
 //
 // gfx950 mapping (bf16 path):
 //  * Transposed products.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K tile from LDS,
-//    B = Q^T held in VGPRs for the whole kernel) puts one query per lane column: lane l holds
+//    B = Q^T held in VGPRs for the whole query block) puts one query per lane column: lane l holds
 //    query l % 32 and 16 of the 32 keys of an MFMA block, the other 16 sit in lane l ^ 32.
 //    Row max and row sum are then in-lane reductions plus one permlane32 swap, and the
 //    rescale factor exp2(m_old - m_new) is a per-lane scalar.
@@ -114,7 +114,6 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
                                           char* vb1, char* stg, bf16x8_t (&qf)[Bf16Cfg<D>::KSTEPS], bool pre,
                                           bool has_next, int nbh, int nkvh, int nqblk) {
   using C = Bf16Cfg<D>;
-  const uint16_t* Qh = Q + (int64_t)bh * Nq * D;
   const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
   const uint16_t* Vh = V + (int64_t)kvh * Nk * D;
 
@@ -125,9 +124,8 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   const int q_wave0 = qblk * C::BR + wave * 32;  // first query of this wave (wave-uniform)
 
   // ---- Q^T fragments (B operand) of this block are already in qf: the previous block (or the
-  // kernel, for the first one) loaded them.  This block loads the next block's once its own last
-  // S product is issued.
-  (void)Qh;
+  // kernel, for the first one) loaded them.  This block loads the next block's (its own again when
+  // none follows) at the start of its last softmax phase, after its last S product.
 
   // ---- the workgroup streams n tiles and every wave processes all of them.  Without a mask the
   // tile order is free, so query blocks of one head start at different tiles (rotation rot):
@@ -160,7 +158,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   }
   // With an even tile count the step past the last tile reloads into kb0; when a next block
   // follows, that load fetches the next block's first K tile instead (it lands in kb0, where the
-  // next block expects it), and the next block's Q is loaded during this block's last phase.
+  // next block expects it), and the next block skips its own first load, wait and barrier.
   const bool do_pf = has_next && (n % 2 == 0);
   const uint16_t* nKh = K + (int64_t)nkvh * Nk * D;
   const int nrot = CAUSAL ? 0 : (int)(((int64_t)nqblk * n) / n_qblk);
@@ -359,7 +357,8 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     wait_loads();
     bar();
   }
-  // Slots by tile parity: K_j in kb[j & 1], V_j in vb[j & 1].  Every wave runs 2n + 3 barriers.
+  // Slots by tile parity: K_j in kb[j & 1], V_j in vb[j & 1].  Every wave runs 2n + 3 barriers
+  // (2n + 2 when the previous block preloaded K_0).
   if (group == 0) {
     issue(Kh, 1, kb1);  // h = 0 (K_1 is a harmless reload of K_0 when n = 1)
     issue(Vh, 0, vb0);
@@ -469,10 +468,10 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
 // same number of tiles and the CUs stay balanced; a non-causal item is one query block, and so
 // is a causal one when pairing would leave CUs idle (fewer pairs than CUs: the blocks then run
 // heaviest first, one per CU, which for a short query chunk against a long cache are nearly
-// equal anyway).  With
-// xcd_split, the items of XCD x (workgroups b with b % 8 == x) are a contiguous range ordered
-// by head, so the 32 CUs of an XCD work on about two heads at a time and share their K/V in
-// that XCD's L2.
+// equal anyway).  With xcd_split, the items of XCD x (workgroups b with b % 8 == x) are a
+// contiguous range ordered by head, so the 32 CUs of an XCD work on about two heads at a time and
+// share their K/V in that XCD's L2.  The workgroup walks its blocks as one sequence, so each block
+// can prefetch the next one's Q fragments and first K tile.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
