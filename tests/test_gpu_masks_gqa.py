@@ -124,6 +124,34 @@ def test_chunked_prefill_workload_sampled():
         assert_parity("bf16", metrics(o_h[0, h][rows], l_h[0, h][rows], o_ref, l_ref), f"{w.name} h={h}")
 
 
+# Shapes where each workgroup of the persistent forward walks several query blocks in sequence, with
+# odd and even tile counts (a block with an even count loads the next block's first K tile; an odd
+# count leaves the next block to load its own), with and without the rotated non-causal tile order.
+SEQUENCES = [
+    _fw("seq_none_nk900_odd", 2, 40, 40, 2048, 900, 128, "bf16", None, seed=51),
+    _fw("seq_none_nk1024_even", 2, 40, 20, 2048, 1024, 128, "bf16", None, seed=52),
+    _fw("seq_tl_nq2048_nk900_mixed", 4, 32, 8, 2048, 900, 128, "bf16", "top_left", seed=53),
+    _fw("seq_br_nq2048_nk2080_odd", 4, 32, 8, 2048, 2080, 128, "bf16", "bottom_right", seed=54),
+    _fw("seq_br_nq2048_nk2144_even_d64", 4, 32, 8, 2048, 2144, 64, "bf16", "bottom_right", seed=55),
+]
+
+
+@pytest.mark.parametrize("w", SEQUENCES, ids=lambda w: w.name)
+def test_block_sequences_sampled(w):
+    """More query blocks than compute units: sampled rows of first, middle and last heads."""
+    host, dev = device_inputs(w)
+    o, lse = _fwd_ex(w, dev)
+    o_h, l_h = from_device(o), from_device(lse)
+    del dev, o, lse
+    grp = w.H // w.kv_heads
+    for i, (b, h) in enumerate([(0, 0), (0, w.H // 2 + 1), (w.B - 1, w.H - 1)]):
+        rows = sample_rows(w.Nq, 160, seed=300 + i)
+        o_ref, l_ref = oracle.attention_head(si.as_f32(w, host["q"][b, h]), si.as_f32(w, host["k"][b, h // grp]),
+                                             si.as_f32(w, host["v"][b, h // grp]), w.scale, w.causal, rows=rows,
+                                             diag=w.diag)
+        assert_parity("bf16", metrics(o_h[b, h][rows], l_h[b, h][rows], o_ref, l_ref), f"{w.name} b={b} h={h}")
+
+
 # ------------------------------------------------------------------------------- decode
 def _dw(name, B, H, Hkv, Nk, d, dtype, S, seed=31):
     return Workload(name, B=B, H=H, H_kv=Hkv, Nq=1, Nk=Nk, d=d, dtype=dtype, causal=False, seed=seed, num_splits=S)
