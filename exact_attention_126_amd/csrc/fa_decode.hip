@@ -28,9 +28,12 @@ __device__ __forceinline__ u32x4_t stream_load16(const void* p) {
   return __builtin_nontemporal_load((const u32x4_t*)p);
 }
 
+// x from lane CTRL-permuted within its row.  Every pattern used here reads a valid lane, so
+// bound_ctrl is set: that lets the compiler fold the move into the add that consumes it
+// (v_add_f32 with a DPP source) instead of issuing a separate v_mov_b32_dpp.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
@@ -98,7 +101,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
 
   float qv[GE][EPL];
 #pragma unroll
-  for (int g = 0; g < GE; ++g) Elt<T>::widen(gload16(Q + (int64_t)(bh0 + g) * D + li * EPL), qv[g]);
+  for (int g = 0; g < GE; ++g) {
+    Elt<T>::widen(gload16(Q + (int64_t)(bh0 + g) * D + li * EPL), qv[g]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[g][e] *= sl2;  // scores come out in log2 units
+  }
   const int kvh = (bh0 / H) * (H / group) + (bh0 % H) / group;  // K/V head shared by the GE query heads
   const T* Kh = K + (int64_t)kvh * Nk * D + li * EPL;
   const T* Vh = V + (int64_t)kvh * Nk * D + li * EPL;
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[g][e], kf[e], dot);
         dot = group_sum<LPK>(dot);
-        sc[u][g] = in ? dot * sl2 : -INFINITY;
+        sc[u][g] = in ? dot : -INFINITY;
         bm[g] = fmaxf(bm[g], sc[u][g]);
       }
     }
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(const uint16_t* _
     Elt<uint16_t>::widen(gload16(qp), qv[g]);
     Elt<uint16_t>::widen(gload16(qp + 8), qv[g] + 8);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[g][e] *= ks;
+    for (int e = 0; e < EPL; ++e) qv[g][e] *= ks * sl2;  // K scale and scores in log2 units
   }
   const uint8_t* Kh = K + (int64_t)kvh * Nk * D + li * EPL;
   const uint8_t* Vh = V + (int64_t)kvh * Nk * D + li * EPL;
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(const uint16_t* _
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[g][e], kf[e], dot);
         dot = group_sum<LPK>(dot);
-        sc[u][g] = in ? dot * sl2 : -INFINITY;
+        sc[u][g] = in ? dot : -INFINITY;
         bm[g] = fmaxf(bm[g], sc[u][g]);
       }
     }
