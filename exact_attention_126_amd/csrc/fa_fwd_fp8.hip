@@ -264,7 +264,10 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
 #pragma unroll
     for (int jj = 2; jj < 15; ++jj) mx = max3f(mx, s1[jj], s0[jj + 1]);
     mx = max3f(mx, s1[15], s1[15]);
-    mx = max_across_halves(mx) * sl2;
+    {  // across the two lane halves, without fmaxf's canonicalising of the swapped values
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1])) * sl2;
+    }
     if (__builtin_amdgcn_ballot_w64(mx > m2 + kTau) != 0) {
       const float mnew = fmaxf(m2, mx);
       const float alpha = fast_exp2(m2 - mnew);
@@ -274,7 +277,7 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
       for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] *= alpha;
     }
     const float nm = kBias - m2;
-    float rs = 0.f;
+    float rs;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const f32x16_t& s = (w < 4) ? s0 : s1;
@@ -283,7 +286,7 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
       const float p1 = fast_exp2(__builtin_fmaf(s[j0 + 1], sl2, nm));
       const float p2 = fast_exp2(__builtin_fmaf(s[j0 + 2], sl2, nm));
       const float p3 = fast_exp2(__builtin_fmaf(s[j0 + 3], sl2, nm));
-      rs += (p0 + p1) + (p2 + p3);
+      rs = w == 0 ? (p0 + p1) + (p2 + p3) : rs + ((p0 + p1) + (p2 + p3));
       int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
       pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
     }
