@@ -51,6 +51,47 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// max / sum of x over lanes l and l ^ W.  W = 16 and 32 stay in the VALU (v_permlane16_swap /
+// v_permlane32_swap hand each lane its partner's value next to its own); smaller W go through
+// the LDS crossbar.  Both operands are commutative, so every form gives the same bits.
+template <int W>
+__device__ __forceinline__ float xor_max(float x) {
+  if constexpr (W == 16 || W == 32) {
+    const auto r = W == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                           : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    return fmaxf(x, __shfl_xor(x, W));
+  }
+}
+template <int W>
+__device__ __forceinline__ float xor_sum(float x) {
+  if constexpr (W == 16 || W == 32) {
+    const auto r = W == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                           : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    return x + __shfl_xor(x, W);
+  }
+}
+// Reduction over the lanes l ^ W, l ^ 2W, ... up to l ^ 32 (the key-row groups of a wave).
+template <int W>
+__device__ __forceinline__ float max_over_groups(float x) {
+  if constexpr (W >= 64) {
+    return x;
+  } else {
+    return max_over_groups<2 * W>(xor_max<W>(x));
+  }
+}
+template <int W>
+__device__ __forceinline__ float sum_over_groups(float x) {
+  if constexpr (W >= 64) {
+    return x;
+  } else {
+    return sum_over_groups<2 * W>(xor_sum<W>(x));
+  }
+}
+
 template <typename T>
 struct Elt;
 template <>
@@ -148,8 +189,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
     }
 #pragma unroll
     for (int g = 0; g < GE; ++g) {
-#pragma unroll
-      for (int w = LPK; w < 64; w <<= 1) bm[g] = fmaxf(bm[g], __shfl_xor(bm[g], w));
+      bm[g] = max_over_groups<LPK>(bm[g]);
       const float mnew = fmaxf(m[g], bm[g]);
       const float alpha = fast_exp2(m[g] - mnew);
       m[g] = mnew;
@@ -173,12 +213,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
   // fold the key groups of the wave: lanes with equal li hold the same dims
 #pragma unroll
   for (int g = 0; g < GE; ++g) {
+    l[g] = sum_over_groups<LPK>(l[g]);
 #pragma unroll
-    for (int w = LPK; w < 64; w <<= 1) {
-      l[g] += __shfl_xor(l[g], w);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], w);
-    }
+    for (int e = 0; e < EPL; ++e) acc[g][e] = sum_over_groups<LPK>(acc[g][e]);
     if (lane == 0) {
       s_m[wave][g] = m[g];
       s_l[wave][g] = l[g];
@@ -305,8 +342,7 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(const uint16_t* _
     }
 #pragma unroll
     for (int g = 0; g < GE; ++g) {
-#pragma unroll
-      for (int w = LPK; w < 64; w <<= 1) bm[g] = fmaxf(bm[g], __shfl_xor(bm[g], w));
+      bm[g] = max_over_groups<LPK>(bm[g]);
       const float mnew = fmaxf(m[g], bm[g]);
       const float alpha = fast_exp2(m[g] - mnew);
       m[g] = mnew;
@@ -329,12 +365,9 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(const uint16_t* _
   }
 #pragma unroll
   for (int g = 0; g < GE; ++g) {
+    l[g] = sum_over_groups<LPK>(l[g]);
 #pragma unroll
-    for (int w = LPK; w < 64; w <<= 1) {
-      l[g] += __shfl_xor(l[g], w);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], w);
-    }
+    for (int e = 0; e < EPL; ++e) acc[g][e] = sum_over_groups<LPK>(acc[g][e]);
     if (lane == 0) {
       s_m[wave][g] = m[g];
       s_l[wave][g] = l[g];
