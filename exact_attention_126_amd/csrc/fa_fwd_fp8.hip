@@ -287,7 +287,9 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
       const float p2 = fast_exp2(__builtin_fmaf(s[j0 + 2], sl2, nm));
       const float p3 = fast_exp2(__builtin_fmaf(s[j0 + 3], sl2, nm));
       rs = w == 0 ? (p0 + p1) + (p2 + p3) : rs + ((p0 + p1) + (p2 + p3));
-      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      // the low half is written here and the high half by the next conversion, so the word's old
+      // contents (the previous tile's codes, already in the register) need no clearing
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb[w], false);
       pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
     }
     lsum += rs;
