@@ -176,7 +176,9 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
   for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] = f32x16_t{};
   float m2 = -INFINITY, lsum = 0.f;
   f32x16_t s0, s1;  // S^T of the current tile, two 32-key blocks
-  i32x8_t pb;       // E4M3 P^T of the previous tile (32 keys per lane-half)
+  // E4M3 P^T of the previous tile (32 keys per lane-half).  Zeroed once per block: the packing
+  // below reads each word (only to overwrite it half by half), so it must never be indeterminate.
+  i32x8_t pb = {};
 
   auto kfrag = [&](const FA_LDS char* kt, int blk, int ks) {
     return join16(lds_load16(kt + blk * 32 * C::RB + koff[ks][0]), lds_load16(kt + blk * 32 * C::RB + koff[ks][1]));
