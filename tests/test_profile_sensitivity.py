@@ -7,8 +7,11 @@ faithful model passes on every profile, and each planted mistake in the rescale 
 at least one profile.  Only the rising and late-spike profiles expose these mistakes (by
 factors of 100 to 27000 over the tolerance); the falling and sawtooth ones never rescale after
 their first tile.  The faithful model uses at most about half of the tolerance (the bf16
-output rounding).  The model is test infrastructure, written from the recurrence of the
-Day-21 page §5.2-5.3 with the lazy threshold; it is not the oracle and not the GPU code."""
+output rounding).  The same is shown for the backward's derived tolerance: a model with its bf16 roundings of P,
+dS and the outputs stays within it on every profile (at most about half), and planted
+mistakes (the row term of dS dropped, dK without the scale, dQ from P instead of dS, dV from dS
+instead of P) exceed it by factors of 35 and more.  The models are test infrastructure, written from the recurrence of the
+Day-21 page §5.2-5.3 with the lazy threshold; they are not the oracle and not the GPU code."""
 import math
 
 import numpy as np
@@ -92,4 +95,51 @@ def test_faithful_model_passes(kind, causal):
 @pytest.mark.parametrize("mistake", ["no_o_rescale", "no_l_rescale", "alpha_sign", "p_uses_old_max"])
 def test_planted_rescale_mistake_is_caught(mistake):
     worst = max(_max_violation(kind, causal, mistake) for kind in PROFILES for causal in (False, True))
+    assert worst > 1.0, (mistake, worst)
+
+
+def _backward_model(f, causal, mistake=None):
+    """float64 gradients with the backward's roundings (P and dS to bf16 before their products,
+    outputs to bf16), optionally with one planted mistake; f holds [1, 2, N, d] float32 arrays."""
+    q, k, v, do = (f[x][0].astype(np.float64) for x in ("q", "k", "v", "do"))
+    s = SCALE * q @ k.transpose(0, 2, 1)
+    if causal:
+        s = np.where(np.arange(k.shape[1])[None, None, :] > np.arange(q.shape[1])[None, :, None], -np.inf, s)
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    o = _bf16(p @ v).astype(np.float64)
+    row = (do * o).sum(-1, keepdims=True)
+    ds = p * (do @ v.transpose(0, 2, 1) - (0.0 if mistake == "no_row_term" else row))
+    pb, dsb = _bf16(p).astype(np.float64), _bf16(ds).astype(np.float64)
+    sc_k = 1.0 if mistake == "dk_unscaled" else SCALE
+    dq = _bf16(SCALE * (pb if mistake == "dq_uses_p" else dsb) @ k)
+    dk = _bf16(sc_k * dsb.transpose(0, 2, 1) @ q)
+    dv = _bf16((dsb if mistake == "dv_uses_ds" else pb).transpose(0, 2, 1) @ do)
+    return {"dq": dq, "dk": dk, "dv": dv}
+
+
+def _backward_violation(kind, causal, mistake=None):
+    from tests.test_gpu_bwd import _rel_l2
+    from tests.test_gpu_softmax_paths import _backward_tolerances
+
+    nq, nk = (330, 330) if causal else (200, 330)
+    q, k, v = _inputs(kind, nq, nk, "bf16")
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([5, 3])))
+    do = g.standard_normal((1, 2, nq, 128)).astype(np.float32)
+    f = {x: _bf16(a) for x, a in zip(("q", "k", "v", "do"), (q, k, v, do))}
+    got = _backward_model(f, causal, mistake)
+    ref = dict(zip(("dq", "dk", "dv"), oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], SCALE, causal)))
+    tol = _backward_tolerances(f, causal)
+    return max(_rel_l2(got[x][None], ref[x]) / tol[x] for x in tol)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", list(PROFILES))
+def test_backward_rounding_model_within_tolerance(kind, causal):
+    assert _backward_violation(kind, causal) <= 1.0
+
+
+@pytest.mark.parametrize("mistake", ["no_row_term", "dk_unscaled", "dq_uses_p", "dv_uses_ds"])
+def test_planted_backward_mistake_is_caught(mistake):
+    worst = max(_backward_violation(kind, causal, mistake) for kind in PROFILES for causal in (False, True))
     assert worst > 1.0, (mistake, worst)
