@@ -7,11 +7,13 @@ faithful model passes on every profile, and each planted mistake in the rescale 
 at least one profile.  Only the rising and late-spike profiles expose these mistakes (by
 factors of 100 to 27000 over the tolerance); the falling and sawtooth ones never rescale after
 their first tile.  The faithful model uses at most about half of the tolerance (the bf16
-output rounding).  The same is shown for the backward's derived tolerance: a model with its bf16 roundings of P,
-dS and the outputs stays within it on every profile (at most about half), and planted
-mistakes (the row term of dS dropped, dK without the scale, dQ from P instead of dS, dV from dS
-instead of P) exceed it by factors of 35 and more.  The models are test infrastructure, written from the recurrence of the
-Day-21 page §5.2-5.3 with the lazy threshold; they are not the oracle and not the GPU code."""
+output rounding).  The same is shown for the backward's derived tolerance: a model with its
+bf16 roundings of P, dS and the outputs stays within it on every profile (at most about half),
+and planted mistakes (the row term of dS dropped, dK without the scale, dQ from P instead of
+dS, dV from dS instead of P) exceed it by factors of 35 and more.  The models are test
+infrastructure: the forward one follows the recurrence of the Day-21 page §5.2-5.3 with the
+lazy threshold, the backward one the chain rule through the definition; neither is the oracle
+or the GPU code."""
 import math
 
 import numpy as np
