@@ -449,7 +449,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               float p = fast_exp2(__builtin_fmaf(s[bl][j], sl2, -l2));
               if constexpr (decltype(mask_tag)::value) {
                 const int qq = q0 + 8 * G + 4 * bl + j;
-                if (qq >= Nq || (CAUSAL && key > qq + diag)) p = 0.f;
+                asm volatile("" : "+v"(p));  // a select, not a branch around the exponential per element
+                p = (qq >= Nq || (CAUSAL && key > qq + diag)) ? 0.f : p;
               }
               pv[e] = p;
               dsv[e] = p * (dp[bl][j] - dr);
