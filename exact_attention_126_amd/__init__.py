@@ -251,10 +251,14 @@ def fa_decode_split_fp8kv(q, k, v, k_scale, v_scale, workspace, num_splits: int,
 
 def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None) -> None:
     """Merge the split partials into o [B,H,1,d] and lse [B,H,1]."""
+    if o.dim() != 4 or o.shape[2] != 1:
+        raise ValueError(f"o {tuple(o.shape)} must be [B,H,1,d]")
+    B, H, _, d = o.shape
+    if tuple(lse.shape) != (B, H, 1):
+        raise ValueError(f"lse {tuple(lse.shape)} must be {(B, H, 1)}")
     _check(workspace, "workspace")
     _check(o, "o")
     _check(lse, "lse", torch.float32)
-    B, H, _, d = o.shape
     st = lib().fa_decode_combine(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(o), _ptr(lse),
                                  B, H, d, int(num_splits), _dtype_code(o), _stream(stream))
     _raise(st, "fa_decode_combine")

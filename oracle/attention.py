@@ -40,14 +40,9 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def scores(q, k, scale: float, causal: bool, row_offset: int = 0) -> np.ndarray:
-    """S = scale * q k^T for query rows row_offset.. (+ causal -inf above the diagonal)."""
-    s = float(scale) * (_f64(q) @ _f64(k).T)
-    if causal:
-        i = np.arange(s.shape[0])[:, None] + row_offset
-        j = np.arange(s.shape[1])[None, :]
-        s = np.where(j > i, -np.inf, s)
-    return s
+def scores(q, k, scale: float) -> np.ndarray:
+    """S = scale * q k^T of one head (no mask)."""
+    return float(scale) * (_f64(q) @ _f64(k).T)
 
 
 def softmax_two_pass(s: np.ndarray):
@@ -100,9 +95,9 @@ def attention(q, k, v, scale: float, causal: bool = False, row_chunk: int = 1024
     return o, lse
 
 
-def attention_probs(q, k, scale: float, causal: bool = False) -> np.ndarray:
-    """The full probability matrix P of one head (small inputs only)."""
-    p, _, _ = softmax_two_pass(scores(q, k, scale, causal))
+def attention_probs(q, k, scale: float) -> np.ndarray:
+    """The full probability matrix P of one head, no mask (small inputs only)."""
+    p, _, _ = softmax_two_pass(scores(q, k, scale))
     return p
 
 

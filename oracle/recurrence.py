@@ -11,6 +11,9 @@ and from the Q31 answer, follow-up 2: merging two partial results rescales the o
 the smaller maximum by exp(m_small - m_large) (its example: maxima 10 and 12, factor exp(-2)).
 
 The initial state is m = -inf, l = 0, so the first block's rescale factor is exp(-inf) = 0.
+
+A plain softmax of a vector x is the special case of one query q = [1], keys [x_j] (d = 1),
+scale 1 and one-hot value rows: the output row is then softmax(x) itself.
 """
 from __future__ import annotations
 
@@ -19,26 +22,6 @@ import math
 
 def _exp(x: float) -> float:
     return 0.0 if x == -math.inf else math.exp(x)
-
-
-def online_softmax(x, block: int):
-    """Softmax of the sequence x computed block by block (Day-21 §5.2).
-
-    The outputs already written are rescaled whenever the running maximum grows.
-    Returns a list of floats.
-    """
-    x = [float(t) for t in x]
-    m, l = -math.inf, 0.0
-    out = []
-    for i in range(0, len(x), block):
-        xb = x[i:i + block]
-        m_new = max(m, max(xb))
-        alpha = _exp(m - m_new)
-        p = [math.exp(t - m_new) for t in xb]
-        l = alpha * l + sum(p)
-        out = [alpha * t for t in out] + p
-        m = m_new
-    return [t / l for t in out]
 
 
 def attention_row(q, keys, values, scale: float, block: int):

@@ -192,6 +192,24 @@ def test_decode_combine_validation(L):
     assert combine(L, wsb=fa.fa_decode_workspace_bytes(2, 3, 64, 4) - 4) == 5
 
 
+def test_binding_combine_checks_output_shapes():
+    """The combine writes B*H LSE values and B*H*d outputs, with B, H and d taken from o: a short
+    lse or an o that is not [B,H,1,d] is rejected before the library is called."""
+    import torch
+    ws = torch.zeros(fa.fa_decode_workspace_bytes(2, 3, 64, 4) // 4)
+    o = torch.zeros(2, 3, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="lse"):
+        fa.fa_decode_combine(ws, o, torch.zeros(2, 2, 1), 4)
+    with pytest.raises(ValueError, match="lse"):
+        fa.fa_decode_combine(ws, o, torch.zeros(6), 4)
+    with pytest.raises(ValueError, match="o "):
+        fa.fa_decode_combine(ws, torch.zeros(2, 3, 2, 64, dtype=torch.bfloat16), torch.zeros(2, 3, 1), 4)
+    with pytest.raises(ValueError, match="o "):
+        fa.fa_decode_combine(ws, torch.zeros(6, 64, dtype=torch.bfloat16), torch.zeros(2, 3, 1), 4)
+    with pytest.raises(ValueError, match="device"):  # right shapes, host memory
+        fa.fa_decode_combine(ws, o, torch.zeros(2, 3, 1), 4)
+
+
 def test_binding_rejects_host_tensors():
     import torch
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)

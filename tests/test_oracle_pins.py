@@ -54,6 +54,21 @@ def test_batched_equals_per_head():
             assert np.array_equal(o[b, h], o1) and np.array_equal(lse[b, h], l1)
 
 
+def test_scores_and_probs_against_pure_python():
+    """scores() and attention_probs() (no mask) against dot products and exponentials written out
+    with Python loops and math.exp on a 5 x 7 head with d = 3; P's rows sum to one."""
+    g = np.random.default_rng(3)
+    q, k = g.standard_normal((5, 3)) * 2, g.standard_normal((7, 3)) * 2
+    s = oracle.scores(q, k, 0.4)
+    p = oracle.attention_probs(q, k, 0.4)
+    for i in range(5):
+        row = [0.4 * sum(q[i, c] * k[j, c] for c in range(3)) for j in range(7)]
+        assert max(abs(a - b) for a, b in zip(row, s[i])) < 1e-14
+        e = [math.exp(t) for t in row]
+        assert max(abs(a / sum(e) - b) for a, b in zip(e, p[i])) < 1e-15
+        assert abs(p[i].sum() - 1.0) < 1e-14
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _variant(q, k, v, scale, causal, *, mistake):
     """A copy of the reference's steps with one planted mistake."""
@@ -114,13 +129,19 @@ def test_recurrence_equals_two_pass_brute_force_grid():
 
 
 def test_day21_exercise_online_softmax():
+    """The exercise's vector softmax, block by block: one query q = [1] against keys [x_j] with
+    one-hot value rows, so the recurrence's output row is softmax(x) itself."""
     ex = _golden("day21_online_softmax_exercise.json")
     x = np.random.default_rng(ex["seed"]).standard_normal(ex["n"]) * ex["std"]
-    online = np.array(recurrence.online_softmax(x, ex["block"]))
-    p, _, _ = oracle.softmax_two_pass(x[None])
-    err = np.abs(online - p[0]).max()
+    n = len(x)
+    one_hot = [[1.0 if r == c else 0.0 for c in range(n)] for r in range(n)]
+    online, lse = recurrence.attention_row([1.0], [[t] for t in x], one_hot, 1.0, ex["block"])
+    p, m, l = oracle.softmax_two_pass(x[None])
+    err = np.abs(np.array(online) - p[0]).max()
     assert err < ex["tolerance"]  # the page's bound
     assert err < 1e-15            # in float64 the two agree to rounding
+    assert abs(sum(online) - 1.0) < 1e-12
+    assert abs(lse - (m[0] + math.log(l[0]))) < 1e-12
 
 
 def test_q31_worked_merge_example():
