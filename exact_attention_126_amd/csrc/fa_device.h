@@ -42,6 +42,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// x rounded to bf16 (the same conversion as pack_bf16x2, round to nearest even) and widened back.
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
+
 // max(a, b, c): lowers to one v_maximum3_f32.  Unlike fmaxf (which first quiets each input the
 // compiler cannot prove canonical, such as MFMA results, with an extra instruction) it needs no
 // canonicalisation; it propagates NaN, and scores are never NaN here.  Being visible to the

@@ -36,7 +36,9 @@
 //    instead of draining every read in flight at each load.
 //  * The running max is raised lazily: the O_acc rescale is skipped unless some row's max grew
 //    by more than 2^8 (the exponentials stay below 256; the result does not depend on the
-//    subtracted value).
+//    subtracted value).  The bf16 rounding of each tile's largest exponential is carried in a
+//    second sum that joins the normaliser of O only, so a key that dominates its row is not
+//    left with that rounding (LSE uses the fp32 sum alone).
 //  * Causal: every wave processes all the tiles its workgroup needs and masks, element by
 //    element, the tiles that reach past its own diagonal (a tile wholly past it contributes
 //    nothing); uniform work keeps the two groups in lockstep.  Query blocks with the most
@@ -198,7 +200,11 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   f32x16_t oacc[C::DBLK];
 #pragma unroll
   for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] = f32x16_t{};
-  float m2 = -INFINITY, lsum = 0.f;
+  // m2: running max used for the exponentials (log2 units); lsum: this lane half's share of the
+  // row sum of the fp32 exponentials (for l and LSE); csum: the bf16 rounding error of each tile's
+  // largest exponential, summed (the same in both lane halves; it joins l only where O is
+  // normalised, see softmax_phase).
+  float m2 = -INFINITY, lsum = 0.f, csum = 0.f;
   f32x16_t s0, s1;  // S^T of the current tile, two 32-key blocks
   u32x4_t pb[4];    // bf16 P^T of the previous tile, four 16-key groups
 
@@ -289,6 +295,12 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // the keys (a tile past the diagonal is masked whole and contributes nothing), running max
   // raised lazily with the O_acc rescale, P_j = exp2(S_j * scale * log2 e - m) packed to bf16,
   // row sums into l.
+  // With the lazy max the tile's largest exponential lies anywhere in (0, 2^8] instead of being
+  // exactly 1, so its bf16 rounding (relative error up to 2^-8) would stay in O: on a row that one
+  // key dominates, O = bf16(p) v / p misses v by up to 2^-8 |v|.  That error of the tile's largest
+  // exponential, bf16(p_max) - p_max, is added to csum, and O is divided by l + csum: the dominant
+  // key's rounding then cancels between O_acc and its normaliser, as if the running max were
+  // exact.  LSE keeps the fp32 sum l.
   auto softmax_phase = [&](int j) {
     const int tile0 = tile_of(j) * C::BC;
     if ((tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag)) {
@@ -305,19 +317,26 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
 #pragma unroll
     for (int jj = 2; jj < 15; ++jj) mx = max3f(mx, s1[jj], s0[jj + 1]);
     mx = max3f(mx, s1[15], s1[15]);
+    float smax;  // the row's largest score in this tile, unscaled
     {  // across the two lane halves, without fmaxf's canonicalising of the swapped values
       const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1])) * sl2;
+      smax = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      mx = smax * sl2;
     }
     if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
       const float mnew = fmaxf(m2, mx);
       const float alpha = fast_exp2(m2 - mnew);
       m2 = mnew;
       lsum *= alpha;
+      csum *= alpha;
 #pragma unroll
       for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] *= alpha;
     }
     const float nm = -m2;
+    {  // the same FMA and exp2 as that key's own exponential below, so the two round alike
+      const float pmax = fast_exp2(__builtin_fmaf(smax, sl2, nm));
+      csum += bf16_round(pmax) - pmax;
+    }
     float rs;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -334,7 +353,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     lsum += rs;
     // Keep this phase's vector work in this phase: without the fence the compiler sinks the
     // exponentials past the barrier, next to their use in the other group's MFMA phase.
-    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum), "+v"(m2));
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum), "+v"(m2), "+v"(csum));
   };
 
   // Workgroup barrier between half-periods.  It waits for this wave's LDS reads (the slot may
@@ -430,7 +449,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   uint16_t* Oh = O + (int64_t)bh * Nq * D;
   float* Lh = LSE + (int64_t)bh * Nq;
   const float l = sum_across_halves(lsum);
-  const float inv = 1.f / l;
+  const float inv = 1.f / (l + csum);
   const int q = q_wave0 + l32;
   // Lane index behind an empty asm: the staging addresses below are derived from it, so the
   // compiler cannot hoist them into the tile loop, where they would hold registers for nothing.

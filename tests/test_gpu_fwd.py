@@ -1,21 +1,17 @@
 """Parity of the fused forward (fa_fwd through the C ABI) with the float64 reference.
 
 Small shapes are compared element by element over the whole output: they span several
-64-key tiles and 128-row query blocks with ragged tails.  The full-size workloads run in the
-same launch configuration the benchmark times and are compared on sampled rows of sampled
-heads, which the reference computes one by one."""
-import math
-
+64-key tiles and 128-row query blocks with ragged tails.  The full-size workloads are compared
+on every head in tests/test_gpu_workloads_all_heads.py."""
 import numpy as np
 import pytest
 import torch
 
 import exact_attention_126_amd as fa
 import oracle
-import synth
 from synth import inputs as si
 from synth.workloads import Workload
-from tests.gpu_util import assert_parity, device_inputs, from_device, metrics, sample_rows
+from tests.gpu_util import assert_parity, device_inputs, from_device, metrics
 
 pytestmark = pytest.mark.gpu
 
@@ -59,50 +55,6 @@ def test_fwd_small_full_compare(w):
     o_ref, l_ref = oracle.attention(si.as_f32(w, host["q"]), si.as_f32(w, host["k"]), si.as_f32(w, host["v"]),
                                     w.scale, w.causal)
     assert_parity(w.dtype, metrics(from_device(o), from_device(lse), o_ref, l_ref), w.name)
-
-
-def test_tiny_f32_workload_full():
-    w = synth.get("tiny_f32_n128_d64")
-    host, dev = device_inputs(w)
-    o, lse = _run(w, dev)
-    o_ref, l_ref = oracle.attention(host["q"], host["k"], host["v"], w.scale, w.causal)
-    assert_parity("f32", metrics(from_device(o), from_device(lse), o_ref, l_ref), w.name)
-
-
-def test_short_batch_workload_heads():
-    """B4 H16 N2048 d64: every row of six heads spread over the batch and head indices."""
-    w = synth.get("batch_b4h16_n2048_d64")
-    host, dev = device_inputs(w)
-    o, lse = _run(w, dev)
-    o_h, l_h = from_device(o), from_device(lse)
-    for b, h in [(0, 0), (0, 15), (1, 7), (2, 3), (3, 0), (3, 15)]:
-        o_ref, l_ref = oracle.attention_head(si.as_f32(w, host["q"][b, h]), si.as_f32(w, host["k"][b, h]),
-                                             si.as_f32(w, host["v"][b, h]), w.scale, w.causal)
-        assert_parity("bf16", metrics(o_h[b, h], l_h[b, h], o_ref, l_ref), f"{w.name} b={b} h={h}")
-
-
-def _sampled_causal_workload(name, heads, nrows):
-    w = synth.get(name)
-    host, dev = device_inputs(w)
-    o, lse = _run(w, dev)
-    o_h, l_h = from_device(o), from_device(lse)
-    del dev, o, lse
-    for i, (b, h) in enumerate(heads):
-        rows = sample_rows(w.Nq, nrows, seed=100 + i)
-        o_ref, l_ref = oracle.attention_head(si.as_f32(w, host["q"][b, h]), si.as_f32(w, host["k"][b, h]),
-                                             si.as_f32(w, host["v"][b, h]), w.scale, w.causal, rows=rows)
-        assert_parity("bf16", metrics(o_h[b, h][rows], l_h[b, h][rows], o_ref, l_ref),
-                      f"{w.name} b={b} h={h} rows={len(rows)}")
-
-
-def test_headline_prefill_sampled():
-    """B8 H16 N8192 d128 causal, K x2: sampled rows of four heads."""
-    _sampled_causal_workload("prefill_b8h16_n8192_d128_causal", [(0, 0), (3, 9), (5, 2), (7, 15)], 384)
-
-
-def test_long_context_sampled():
-    """B1 H32 N16384 d128 causal, every 64th key row x8: sampled rows of three heads."""
-    _sampled_causal_workload("long_b1h32_n16384_d128_causal", [(0, 0), (0, 17), (0, 31)], 384)
 
 
 def test_lse_matches_log_of_row_sum_identity():

@@ -6,18 +6,17 @@ Small shapes are compared element by element over the whole output (ragged tiles
 Nq > Nk, one query, several group sizes).  Grouped heads must give bit-for-bit what the same
 kernel gives on K/V with each head repeated, and the extended entry points with H_kv = H must
 give bit-for-bit what fa_fwd / fa_decode_split give.  The full-size chunked-prefill and grouped
-decode workloads run as the benchmark times them and are compared on sampled rows and heads."""
+decode workloads, and shapes with more query blocks than compute units, are compared on every
+head in tests/test_gpu_workloads_all_heads.py."""
 
-import numpy as np
 import pytest
 import torch
 
 import exact_attention_126_amd as fa
 import oracle
-import synth
 from synth import inputs as si
 from synth.workloads import Workload
-from tests.gpu_util import assert_parity, device_inputs, from_device, metrics, sample_rows
+from tests.gpu_util import assert_parity, device_inputs, from_device, metrics
 
 pytestmark = pytest.mark.gpu
 
@@ -107,51 +106,6 @@ def test_bottom_right_equals_top_left_when_square_bitwise():
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
 
 
-def test_chunked_prefill_workload_sampled():
-    """B1 H32 H_kv8 Nq2048 Nk16384 d128, bottom-right causal, as the benchmark times it:
-    sampled rows of four heads (two sharing one K/V head)."""
-    w = synth.get("chunk_prefill_b1h32kv8_nq2048_nk16384_d128")
-    host, dev = device_inputs(w)
-    o, lse = _fwd_ex(w, dev)
-    o_h, l_h = from_device(o), from_device(lse)
-    del dev, o, lse
-    grp = w.H // w.kv_heads
-    for i, h in enumerate([0, 1, 17, 31]):
-        rows = sample_rows(w.Nq, 256, seed=200 + i)
-        o_ref, l_ref = oracle.attention_head(si.as_f32(w, host["q"][0, h]), si.as_f32(w, host["k"][0, h // grp]),
-                                             si.as_f32(w, host["v"][0, h // grp]), w.scale, True, rows=rows,
-                                             diag=w.diag)
-        assert_parity("bf16", metrics(o_h[0, h][rows], l_h[0, h][rows], o_ref, l_ref), f"{w.name} h={h}")
-
-
-# Shapes where each workgroup of the persistent forward walks several query blocks in sequence, with
-# odd and even tile counts (a block with an even count loads the next block's first K tile; an odd
-# count leaves the next block to load its own), with and without the rotated non-causal tile order.
-SEQUENCES = [
-    _fw("seq_none_nk900_odd", 2, 40, 40, 2048, 900, 128, "bf16", None, seed=51),
-    _fw("seq_none_nk1024_even", 2, 40, 20, 2048, 1024, 128, "bf16", None, seed=52),
-    _fw("seq_tl_nq2048_nk900_mixed", 4, 32, 8, 2048, 900, 128, "bf16", "top_left", seed=53),
-    _fw("seq_br_nq2048_nk2080_odd", 4, 32, 8, 2048, 2080, 128, "bf16", "bottom_right", seed=54),
-    _fw("seq_br_nq2048_nk2144_even_d64", 4, 32, 8, 2048, 2144, 64, "bf16", "bottom_right", seed=55),
-]
-
-
-@pytest.mark.parametrize("w", SEQUENCES, ids=lambda w: w.name)
-def test_block_sequences_sampled(w):
-    """More query blocks than compute units: sampled rows of first, middle and last heads."""
-    host, dev = device_inputs(w)
-    o, lse = _fwd_ex(w, dev)
-    o_h, l_h = from_device(o), from_device(lse)
-    del dev, o, lse
-    grp = w.H // w.kv_heads
-    for i, (b, h) in enumerate([(0, 0), (0, w.H // 2 + 1), (w.B - 1, w.H - 1)]):
-        rows = sample_rows(w.Nq, 160, seed=300 + i)
-        o_ref, l_ref = oracle.attention_head(si.as_f32(w, host["q"][b, h]), si.as_f32(w, host["k"][b, h // grp]),
-                                             si.as_f32(w, host["v"][b, h // grp]), w.scale, w.causal, rows=rows,
-                                             diag=w.diag)
-        assert_parity("bf16", metrics(o_h[b, h][rows], l_h[b, h][rows], o_ref, l_ref), f"{w.name} b={b} h={h}")
-
-
 # ------------------------------------------------------------------------------- decode
 def _dw(name, B, H, Hkv, Nk, d, dtype, S, seed=31):
     return Workload(name, B=B, H=H, H_kv=Hkv, Nq=1, Nk=Nk, d=d, dtype=dtype, causal=False, seed=seed, num_splits=S)
@@ -190,20 +144,3 @@ def test_decode_grouped_equals_repeated_bitwise():
     o2, l2 = fa.decode(dev["q"], rep["k"], rep["v"], w.num_splits, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
-
-
-def test_decode_gqa_workload_sampled_heads():
-    """B16 H32 H_kv8 Nk32768 d128, 64 splits, as the benchmark times it: 24 sampled heads."""
-    w = synth.get("decode_gqa_b16h32kv8_nk32768_d128")
-    host, dev = device_inputs(w)
-    o, lse = _decode_ex(w, dev)
-    o_h, l_h = from_device(o), from_device(lse)
-    grp = w.H // w.kv_heads
-    g = np.random.default_rng(6)
-    heads = [(0, 0), (15, 31), (3, 4), (3, 7)] + [tuple(x) for x in zip(g.integers(0, 16, 20), g.integers(0, 32, 20))]
-    o_s, l_s, r_o, r_l = [], [], [], []
-    for b, h in heads:
-        ro, rl = oracle.attention_head(si.as_f32(w, host["q"][b, h]), si.as_f32(w, host["k"][b, h // grp]),
-                                       si.as_f32(w, host["v"][b, h // grp]), w.scale, False)
-        o_s.append(o_h[b, h]); l_s.append(l_h[b, h]); r_o.append(ro); r_l.append(rl)
-    assert_parity("bf16", metrics(np.stack(o_s), np.stack(l_s), np.stack(r_o), np.stack(r_l)), w.name)
