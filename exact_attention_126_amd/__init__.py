@@ -25,9 +25,12 @@ FA_MASK_CAUSAL_BOTTOM_RIGHT = 2
 MASKS = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "causal_bottom_right": FA_MASK_CAUSAL_BOTTOM_RIGHT}
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE", 4: "FA_ERR_UNSUPPORTED",
-                5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
+                5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG", 8: "FA_ERR_SCRATCH"}
+# Size of the fixed device scratch behind fa_decode_noalloc (FA_DECODE_NOALLOC_SCRATCH_BYTES)
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTED = ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_split_ex",
-            "fa_decode_split_fp8kv", "fa_decode_combine", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string"]
+            "fa_decode_split_fp8kv", "fa_decode_combine", "fa_decode_noalloc", "fa_bwd_workspace_bytes", "fa_bwd",
+            "fa_status_string"]
 
 _lib = None
 
@@ -63,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.fa_decode_split.restype = i32
         L.fa_decode_combine.argtypes = [vp, ctypes.c_size_t, vp, vp, i64, i64, i64, i32, i32, vp]
         L.fa_decode_combine.restype = i32
+        L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+        L.fa_decode_noalloc.restype = i32
         L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, i64, i32,
@@ -262,6 +267,29 @@ def fa_decode_combine(workspace, o, lse, num_splits: int, stream=None) -> None:
     st = lib().fa_decode_combine(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(o), _ptr(lse),
                                  B, H, d, int(num_splits), _dtype_code(o), _stream(stream))
     _raise(st, "fa_decode_combine")
+
+
+def fa_decode_noalloc(q, k, v, o, lse, num_splits: int, scale: float | None = None, stream=None) -> None:
+    """One-token decode, split and combine, with the partials in the library's fixed device scratch
+    instead of a workspace (nothing is allocated): q [B,H,1,d], k/v [B,H_kv,Nk,d], o [B,H,1,d],
+    lse [B,H,1] float32.  Calls that overlap on one GPU share the scratch and race."""
+    if o.dim() != 4 or tuple(o.shape) != tuple(q.shape):
+        raise ValueError(f"o {tuple(o.shape)} must have the shape of q {tuple(q.shape)}")
+    if q.dim() != 4 or tuple(lse.shape) != (q.shape[0], q.shape[1], 1):
+        raise ValueError(f"lse {tuple(lse.shape)} must be [B,H,1] for q {tuple(q.shape)}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, n, q.dtype)
+    _check(lse, "lse", torch.float32)
+    _check_shapes(q, k, v, same_heads=False)
+    if q.shape[2] != 1:
+        raise ValueError(f"decode takes one query token per head, q is {tuple(q.shape)}")
+    B, H, _, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, H_kv, Nk, d, float(scale),
+                                 int(num_splits), _dtype_code(q), _stream(stream))
+    _raise(st, "fa_decode_noalloc")
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, Nq: int) -> int:

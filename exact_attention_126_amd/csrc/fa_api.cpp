@@ -7,6 +7,8 @@
 
 #include "fa_launch.h"
 
+static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_SCRATCH_BYTES, "scratch size in fa.h and fa_launch.h");
+
 namespace {
 
 constexpr int64_t kI32Max = 2147483647;
@@ -143,6 +145,33 @@ fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, voi
                                          : fa::launch_decode_combine_f32(a, stream));
 }
 
+fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                              int64_t H, int64_t H_kv, int64_t Nk, int64_t d, float scale, int num_splits,
+                              fa_dtype_t dtype, hipStream_t stream) {
+  // Everything is validated before the first HIP call, the scratch address lookup included.
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!dtype_ok(dtype) || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Nk <= 0 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (!head_fits(Nk, d, dtype) || B > kI32Max / H) return FA_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > Nk || !scale_ok(scale)) return FA_ERR_ARG;
+  if (B * H > kI32Max / num_splits) return FA_ERR_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (need > FA_DECODE_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (fa::decode_scratch_address(&ws) != hipSuccess) return FA_ERR_HIP;
+  float* o_part = static_cast<float*>(ws);
+  float* ml = o_part + (size_t)(B * H * num_splits) * (size_t)d;
+  const bool bf16 = dtype == FA_DTYPE_BF16;
+  fa::DecodeSplitArgs sa{q, k, v, o_part, ml, (int)B, (int)H, (int)Nk, (int)d, num_splits, (int)H_kv, scale};
+  const fa_status_t st = from_hip(bf16 ? fa::launch_decode_split_bf16(sa, stream)
+                                       : fa::launch_decode_split_f32(sa, stream));
+  if (st != FA_OK) return st;
+  fa::DecodeCombineArgs ca{o_part, ml, o, lse, (int)B, (int)H, (int)d, num_splits};
+  return from_hip(bf16 ? fa::launch_decode_combine_bf16(ca, stream) : fa::launch_decode_combine_f32(ca, stream));
+}
+
 fa_status_t fa_decode_split_fp8kv(const void* q, const void* k, const void* v, const float* k_scale,
                                   const float* v_scale, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
                                   int64_t H_kv, int64_t Nk, int64_t d, float scale, int num_splits,
@@ -207,6 +236,8 @@ const char* fa_status_string(fa_status_t s) {
     case FA_ERR_HIP: return "HIP runtime error at launch";
     case FA_ERR_ARG:
       return "invalid scalar argument (scale must be finite and > 0; 1 <= num_splits <= Nk; known mask)";
+    case FA_ERR_SCRATCH:
+      return "decode partials larger than the fixed scratch of fa_decode_noalloc (FA_DECODE_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -16,6 +16,8 @@
 // read of the K/V rows.  The four waves' states are merged through LDS and written to the
 // workspace as (O_part, m, l) per query head.
 // decode_combine_kernel: one workgroup per (batch*head), one thread per dim.
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -503,6 +505,34 @@ hipError_t launch_decode_combine_bf16(const DecodeCombineArgs& a, hipStream_t st
 }
 hipError_t launch_decode_combine_f32(const DecodeCombineArgs& a, hipStream_t stream) {
   return combine_impl<float>(a, stream);
+}
+
+// ---- fixed scratch of fa_decode_noalloc, for callers that cannot allocate
+// The split partials live in this array instead of a caller's workspace.  Each device that loads
+// the library holds its own copy, at its own address, until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it only names a stand-in): the device address
+// is looked up once per device and that address is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev].store(p, std::memory_order_release);  // two racing first calls store the same address
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace fa

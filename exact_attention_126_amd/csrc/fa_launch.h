@@ -7,6 +7,9 @@
 
 namespace fa {
 
+// Size of the fixed device scratch behind fa_decode_noalloc (its split partials).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -97,5 +100,7 @@ hipError_t launch_decode_combine_f32(const DecodeCombineArgs& a, hipStream_t str
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_split_fp8kv(const DecodeSplitFp8Args& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream);
+// Device address of the fixed decode scratch on the current device (looked up on first use).
+hipError_t decode_scratch_address(void** out);
 
 }  // namespace fa

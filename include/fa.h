@@ -20,6 +20,8 @@
  *   - scale must be finite and > 0 (1/sqrt(d) in the pages).
  *   - Every pointer is DEVICE memory owned by the caller.  The library allocates nothing,
  *     keeps no global mutable state, prints nothing, and is safe to call from several threads.
+ *     The one exception is fa_decode_noalloc, which uses a fixed scratch array the library
+ *     holds per device (see there).
  *   - Work is enqueued on `stream` (NULL = the default stream); calls return without
  *     synchronising.  Inputs must stay valid and unmodified until the work completes.
  *   - Errors: arguments are validated on the host before any HIP call; on any error nothing is
@@ -59,8 +61,10 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 4, /* d not in {64, 128}, unknown dtype, or fp32 in the backward */
   FA_ERR_WORKSPACE = 5,   /* workspace smaller than fa_decode_workspace_bytes() / fa_bwd_workspace_bytes() */
   FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
-  FA_ERR_ARG = 7          /* scale not finite and > 0, num_splits outside [1, Nk], or an unknown
+  FA_ERR_ARG = 7,         /* scale not finite and > 0, num_splits outside [1, Nk], or an unknown
                              fa_mask_t */
+  FA_ERR_SCRATCH = 8      /* fa_decode_noalloc: the split partials, fa_decode_workspace_bytes(B, H, d,
+                             num_splits) bytes, exceed FA_DECODE_NOALLOC_SCRATCH_BYTES */
 } fa_status_t;
 
 /*
@@ -145,6 +149,29 @@ fa_status_t fa_decode_split_ex(const void* q, const void* k, const void* v,
 fa_status_t fa_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse,
                               int64_t B, int64_t H, int64_t d, int num_splits,
                               fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * One-token decode that allocates nothing: for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  It is
+ * fa_decode_split_ex followed by fa_decode_combine on the same stream, with the same kernels and
+ * the same results bit for bit, except that the split partials go to a fixed scratch array that
+ * the library holds in device memory instead of a caller's workspace.
+ *   q [B,H,1,d], k and v [B,H_kv,Nk,d] (in); o [B,H,1,d] (dtype) and lse [B,H,1] float32 (out).
+ *   Requires fa_decode_workspace_bytes(B, H, d, num_splits) <= FA_DECODE_NOALLOC_SCRATCH_BYTES
+ *   (32 MiB; e.g. B16 H32 d128 with 64 splits needs 17.0 MB), else FA_ERR_SCRATCH and nothing is
+ *   launched.  Other errors as for fa_decode_split_ex, plus o (16 bytes) and lse (4 bytes)
+ *   alignment.  `stream` must belong to the current device.
+ *   Unlike the other entry points, this one keeps state: each GPU holds one 32 MiB scratch array
+ *   from the library's load until the process ends, and the library remembers its address per
+ *   device after the first call there.  Every call on a GPU shares that GPU's array, so calls
+ *   that overlap on one GPU (on different streams, or from different threads without ordering)
+ *   race and give wrong results; calls ordered on one stream are safe.  Nothing in the scratch
+ *   needs clearing: every call writes all the partials it reads.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t H_kv, int64_t Nk, int64_t d, float scale,
+                              int num_splits, fa_dtype_t dtype, hipStream_t stream);
 
 /*
  * Split step of decode against an FP8 KV cache (KV-cache quantisation, which the Day-21 page's

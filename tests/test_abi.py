@@ -47,7 +47,7 @@ def test_single_hip_runtime_mapped(L):
 
 
 def test_status_strings(L):
-    for code in range(8):
+    for code in range(9):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -190,6 +190,29 @@ def test_decode_combine_validation(L):
     assert combine(L, H=0) == 3
     assert combine(L, S=0, wsb=1 << 20) == 7
     assert combine(L, wsb=fa.fa_decode_workspace_bytes(2, 3, 64, 4) - 4) == 5
+
+
+def noalloc(L, q=P, k=P, v=P, o=P, lse=P, B=2, H=4, H_kv=2, Nk=1000, d=128, scale=0.125, S=16, dtype=BF16):
+    vp = ctypes.c_void_p
+    return L.fa_decode_noalloc(vp(q) if q else None, vp(k) if k else None, vp(v) if v else None,
+                               vp(o) if o else None, vp(lse) if lse else None, B, H, H_kv, Nk, d, scale, S, dtype,
+                               None)
+
+
+def test_decode_noalloc_validation(L):
+    """Every check, the scratch limit included, is taken before the first HIP call."""
+    assert noalloc(L, q=0) == 1 and noalloc(L, o=0) == 1 and noalloc(L, lse=0) == 1
+    assert noalloc(L, d=96) == 4 and noalloc(L, dtype=3) == 4
+    assert noalloc(L, o=P + 8) == 2 and noalloc(L, lse=P + 2) == 2 and noalloc(L, k=P_MIS) == 2
+    assert noalloc(L, H=3) == 3 and noalloc(L, B=0) == 3 and noalloc(L, Nk=0) == 3
+    assert noalloc(L, S=0) == 7 and noalloc(L, S=1001) == 7 and noalloc(L, scale=float("nan")) == 7
+    # the largest split count whose partials fit the 32 MiB scratch, and one more
+    B, H, d = 16, 32, 128
+    s_max = fa.DECODE_NOALLOC_SCRATCH_BYTES // (B * H * (d + 2) * 4)
+    assert fa.fa_decode_workspace_bytes(B, H, d, s_max) <= fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_bytes(B, H, d, s_max + 1) > fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert noalloc(L, B=B, H=H, H_kv=H, Nk=32768, d=d, S=s_max + 1) == 8
+    assert noalloc(L, B=1024, H=64, H_kv=8, Nk=32768, d=128, S=64) == 8
 
 
 def test_binding_combine_checks_output_shapes():
