@@ -40,9 +40,11 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
-PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP/clk
-PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+import roofline  # noqa: E402  (MI355X peaks and the algorithmic work and byte models)
+
+PEAK_BF16_TFLOPS = roofline.PEAK_BF16_MFMA_TFLOPS
+PEAK_FP8_TFLOPS = roofline.PEAK_FP8_MFMA_TFLOPS
+PEAK_HBM_GBS = roofline.PEAK_HBM_GBS
 PREFILL = "prefill_b8h16_n8192_d128_causal"
 DECODE = "decode_b16h32_nk32768_d128"
 FWD_SOURCES = ["exact_attention_126_amd/csrc/fa_fwd.hip", "exact_attention_126_amd/csrc/fa_device.h",

@@ -1,4 +1,5 @@
-"""Algorithmic work, byte counts and MI355X peaks used to place the kernels on a roofline.
+"""Algorithmic work, byte counts and MI355X peaks used to place the kernels on a roofline
+(measurement only: the benchmark and the tests use it, the library does not).
 
 Conventions:
   * attention FLOPs = 4 * B * H * Nq * Nk * d (two dense contractions, Q K^T and P V, at
@@ -13,6 +14,7 @@ from __future__ import annotations
 
 # MI355X published peaks.
 PEAK_BF16_MFMA_TFLOPS = 2516.6  # dense: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_FP8_MFMA_TFLOPS = 5033.2   # dense: 256 CU x 2.4 GHz x 8192 FLOP/clk/CU
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 CUS = 256

@@ -7,7 +7,7 @@ import numpy as np
 
 import synth
 from synth import inputs as si
-from exact_attention_126_amd import roofline as rl
+import roofline as rl
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
