@@ -25,6 +25,12 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def L():
+    # FA_ABI_TEST_LIB: another build of the same C ABI to run these cases against (the host-only
+    # sanitizer build of tests/test_host_sanitizer.py)
+    other = os.environ.get("FA_ABI_TEST_LIB")
+    if other:
+        fa._lib = None
+        fa.LIB_PATH = other
     if not os.path.exists(fa.LIB_PATH):
         pytest.fail("libfa.so is not built (python -m exact_attention_126_amd.build)")
     return fa.lib()
