@@ -269,6 +269,29 @@ def time_extras(torch, fa, si, get, reps: int = 20) -> dict:
                               "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4),
                               "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
     del dev, o, lse
+    # the element-mask forward on packed documents (causal inside each document)
+    import numpy as np
+    from synth import masks
+    w = get("masked_docs_b4h16_n8192_d128")
+    allowed = masks.element_mask(w)
+    pairs = masks.visible_pairs(allowed)
+    blocks = allowed.reshape(w.Nq // 256, 256, w.Nk // 64, 64)
+    t_any, t_all = blocks.any(axis=(1, 3)), blocks.all(axis=(1, 3))
+    md = torch.from_numpy(masks.pack_bits(allowed).view(np.int64)).cuda()
+    dev = {x: to_device(w, si.make_tensor(w, x)) for x in "qkv"}
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_fwd_masked_workspace_bytes(w.Nq, w.Nk), dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: fa.fa_fwd_masked(dev["q"], dev["k"], dev["v"], o, lse, md, ws, w.scale, stream=stream),
+               reps, 3)
+    tf = 4.0 * w.B * w.H * pairs * w.d / (ms * 1e-3) / 1e12
+    out["masked_documents"] = {
+        "workload": w.name, "entry": "fa_fwd_masked (tile classification + forward)", "value": round(tf, 1),
+        "unit": "TFLOP/s (4 d FLOP per visible query-key pair)", "ms": round(ms, 4),
+        "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+        "visible_fraction": round(pairs / (w.Nq * w.Nk), 4),
+        "tiles_256x64": {"empty": int((~t_any).sum()), "full": int(t_all.sum()), "partial": int((t_any & ~t_all).sum())}}
+    del dev, o, lse, ws, md
     w = get("decode_gqa_b16h32kv8_nk32768_d128")
     dev = {x: to_device(w, si.make_tensor(w, x)) for x in "qkv"}
     ws = fa.decode_workspace(dev["q"], w.num_splits)

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAP
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG", 8: "FA_ERR_SCRATCH"}
 # Size of the fixed device scratch behind fa_decode_noalloc (FA_DECODE_NOALLOC_SCRATCH_BYTES)
 DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
-EXPORTED = ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_split_ex",
+EXPORTED = ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_masked_workspace_bytes", "fa_fwd_masked", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_split_ex",
             "fa_decode_split_fp8kv", "fa_decode_combine", "fa_decode_noalloc", "fa_bwd_workspace_bytes", "fa_bwd",
             "fa_status_string"]
 
@@ -66,6 +66,11 @@ def lib() -> ctypes.CDLL:
         L.fa_decode_split.restype = i32
         L.fa_decode_combine.argtypes = [vp, ctypes.c_size_t, vp, vp, i64, i64, i64, i32, i32, vp]
         L.fa_decode_combine.restype = i32
+        L.fa_fwd_masked_workspace_bytes.argtypes = [i64, i64]
+        L.fa_fwd_masked_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, ctypes.c_size_t, f32,
+                                    i32, vp]
+        L.fa_fwd_masked.restype = i32
         L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
         L.fa_decode_noalloc.restype = i32
         L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
@@ -157,6 +162,34 @@ def fa_fwd_ex(q, k, v, o, lse, mask=FA_MASK_NONE, scale: float | None = None, st
     st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, H_kv, Nq, Nk, d, m, float(scale),
                          _dtype_code(q), _stream(stream))
     _raise(st, "fa_fwd_ex")
+
+
+def fa_fwd_masked_workspace_bytes(Nq: int, Nk: int) -> int:
+    return int(lib().fa_fwd_masked_workspace_bytes(Nq, Nk))
+
+
+def fa_fwd_masked(q, k, v, o, lse, mask, workspace, scale: float | None = None, stream=None) -> None:
+    """Forward with an element mask: mask [Nq, ceil(Nk/64)] 64-bit words (int64 or uint64 device
+    tensor; bit j % 64 of word [i][j // 64] set iff key j is visible to query row i), shared by every
+    batch and head; workspace of fa_fwd_masked_workspace_bytes(Nq, Nk) bytes.  k, v may have fewer
+    heads than q (grouped heads, as fa_fwd_ex)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, n, q.dtype)
+    _check(lse, "lse", torch.float32)
+    _check(workspace, "workspace")
+    _check_shapes(q, k, v, o, lse, same_heads=False)
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    _check(mask, "mask")
+    if mask.dtype not in (torch.int64, torch.uint64) or tuple(mask.shape) != (Nq, (Nk + 63) // 64):
+        raise ValueError(f"mask must be [Nq, ceil(Nk/64)] = {(Nq, (Nk + 63) // 64)} 64-bit words, got "
+                         f"{tuple(mask.shape)} {mask.dtype}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, H_kv, Nq, Nk, d, _ptr(mask),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), float(scale),
+                             _dtype_code(q), _stream(stream))
+    _raise(st, "fa_fwd_masked")
 
 
 def _check_codes(t, name):
@@ -331,6 +364,16 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=
     else:
         fa_fwd_ex(q, k, v, o, lse, (FA_MASK_CAUSAL if causal else FA_MASK_NONE) if mask is None else mask, scale,
                   stream)
+    return o, lse
+
+
+def attention_masked(q, k, v, mask, scale: float | None = None, stream=None):
+    """(o, lse) = fa_fwd_masked with freshly allocated outputs and workspace."""
+    B, H, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(16, fa_fwd_masked_workspace_bytes(Nq, k.shape[2])), dtype=torch.uint8, device=q.device)
+    fa_fwd_masked(q, k, v, o, lse, mask, ws, scale, stream)
     return o, lse
 
 

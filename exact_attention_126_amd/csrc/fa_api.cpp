@@ -110,6 +110,43 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, const float*
   return from_hip(fa::launch_fwd_fp8(a, stream));
 }
 
+size_t fa_fwd_masked_workspace_bytes(int64_t Nq, int64_t Nk) {
+  if (Nq <= 0 || Nk <= 0 || Nk > (int64_t)fa::kMaxMaskTiles * 64 || Nq > kI32Max) return 0;
+  const int64_t n_qblk = (Nq + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows, nT = (Nk + 63) / 64;
+  return (size_t)((4 * n_qblk + 15) / 16 * 16 + 2 * n_qblk * nT);
+}
+
+fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                          int64_t H_kv, int64_t Nq, int64_t Nk, int64_t d, const uint64_t* mask, void* workspace,
+                          size_t workspace_bytes, float scale, fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !mask || !workspace) return FA_ERR_NULL;
+  if (dtype != FA_DTYPE_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(mask, 8) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Nq <= 0 || Nk <= 0 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (Nk > (int64_t)fa::kMaxMaskTiles * 64) return FA_ERR_SHAPE;  // the block's tile list lives in LDS
+  if (!head_fits(Nq, d, dtype) || !head_fits(Nk, d, dtype)) return FA_ERR_SHAPE;
+  if (B > kI32Max / H || B * H > kI32Max / ((Nq + 31) / 32)) return FA_ERR_SHAPE;
+  const int64_t nT = (Nk + 63) / 64;
+  if (Nq > kI32Max / nT) return FA_ERR_SHAPE;  // mask word offsets
+  if (!scale_ok(scale)) return FA_ERR_ARG;
+  if (workspace_bytes < fa_fwd_masked_workspace_bytes(Nq, Nk)) return FA_ERR_WORKSPACE;
+  int dev = 0, num_cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cus <= 0)
+    return FA_ERR_HIP;
+  const int n_qblk = (int)((Nq + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows);
+  int* counts = static_cast<int*>(workspace);
+  uint16_t* lists = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + (4 * n_qblk + 15) / 16 * 16);
+  fa::MaskClassifyArgs ca{mask, (int)Nq, (int)Nk, (int)nT, fa::kFwdBlockRows, n_qblk, counts, lists};
+  fa_status_t st = from_hip(fa::launch_mask_classify(ca, stream));
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, (int)B, (int)H, (int)Nq, (int)Nk, (int)d, (int)H_kv, false, 0, scale, num_cus,
+                counts, lists, mask, (int)nT};
+  return from_hip(fa::launch_fwd_bf16_masked(a, stream));
+}
+
 size_t fa_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int num_splits) {
   if (B <= 0 || H <= 0 || d <= 0 || num_splits <= 0) return 0;
   if (B > kI32Max / H || B * H > kI32Max / num_splits) return 0;

@@ -77,6 +77,18 @@ struct Bf16Cfg {
   };
 };
 
+// The masked forward's view of its tile classification (mask_classify_kernel): per query block
+// the count and the key-ordered list of non-empty 64-key tiles, bit 15 set on a partial one; the
+// bit-packed element mask (one 64-bit word per query row and tile); and the LDS copy of the
+// current block's list.  Unused (null) without a mask.
+struct MaskView {
+  const int* counts;
+  const uint16_t* lists;
+  const uint64_t* words;
+  int nT;        // 64-key tiles per row, ceil(Nk / 64)
+  uint16_t* tl;  // LDS, kMaxMaskTiles entries
+};
+
 // Lazy rescaling threshold, log2 units: the running max used for the exponentials is only
 // raised when a tile's row max exceeds it by more than this, so most tiles skip the
 // O_acc rescale.  Exponentials are then bounded by 2^kLazyRescale (exact: softmax does not
@@ -108,13 +120,13 @@ __device__ __forceinline__ void load_q_frags(bf16x8_t (&qf)[Bf16Cfg<D>::KSTEPS],
 // One query block (batch*head bh, rows qblk*BR ..) of the forward, run by the whole workgroup
 // with the LDS rings kb0/kb1 (K) and vb0/vb1 (V).  The first barrier it executes orders its LDS
 // use after the previous block's; its last barrier is passed only when every wave is done.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                           float* __restrict__ LSE, int Nq, int Nk, float sl2, int bh, int kvh,
                                           int diag, int qblk, int n_qblk, char* kb0, char* kb1, char* vb0,
                                           char* vb1, char* stg, bf16x8_t (&qf)[Bf16Cfg<D>::KSTEPS], bool pre,
-                                          bool has_next, int nbh, int nkvh, int nqblk) {
+                                          bool has_next, int nbh, int nkvh, int nqblk, const MaskView& mk) {
   using C = Bf16Cfg<D>;
   const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
   const uint16_t* Vh = V + (int64_t)kvh * Nk * D;
@@ -134,13 +146,48 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // the workgroups working on a head then stream different parts of its K/V at any moment
   // instead of all asking the L2 for the same lines.  Step t visits tile (t + rot) mod n; the
   // extra step t = n (a dummy reload of the free slot) maps to a valid tile too.
-  const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR + diag) : Nk;
-  const int n = (kv_end + C::BC - 1) / C::BC;
-  const int rot = CAUSAL ? 0 : (int)(((int64_t)qblk * n) / n_qblk);
+  // With a mask the block walks its list of non-empty tiles in key order instead (copied to LDS
+  // here, read after the block's first barrier); its first entry is read from global memory for
+  // the load issued before that barrier.  Tile indices are wave-uniform and kept in scalars.
+  int n, rot = 0, first_tile = 0;
+  if constexpr (MASKED) {
+    const uint16_t* lst = mk.lists + (int64_t)qblk * mk.nT;
+    n = __builtin_amdgcn_readfirstlane(mk.counts[qblk]);
+    if (n > 0) first_tile = __builtin_amdgcn_readfirstlane((int)(lst[0] & 0x7FFF));
+    for (int i = tid; i < n; i += C::THREADS) mk.tl[i] = lst[i];
+  } else {
+    const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR + diag) : Nk;
+    n = (kv_end + C::BC - 1) / C::BC;
+    rot = CAUSAL ? 0 : (int)(((int64_t)qblk * n) / n_qblk);
+  }
   auto tile_of = [&](int t) {
-    const int x = t + rot;
-    return x >= n ? x - n : x;
+    if constexpr (MASKED) {
+      return (t == 0 || t >= n) ? first_tile : __builtin_amdgcn_readfirstlane((int)(mk.tl[t] & 0x7FFF));
+    } else {
+      const int x = t + rot;
+      return x >= n ? x - n : x;
+    }
   };
+  // a partial tile of the mask: some of its keys are visible to some rows of the block
+  auto partial = [&](int t) { return MASKED && __builtin_amdgcn_readfirstlane((int)mk.tl[t]) >= 0x8000; };
+
+  if constexpr (MASKED) {
+    if (n == 0) {
+      // No row of the block sees any key: O = 0 and LSE = ln 0 = -inf.  The next block's Q
+      // fragments are loaded here, as a block with tiles would in its last phase.
+      load_q_frags<D>(qf, Q, nbh, Nq, nqblk * C::BR + wave * 32, l32, hh);
+      uint16_t* Oh = O + (int64_t)bh * Nq * D;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 32 * C::RB / 1024; ++i) {
+        const int flat = i * 1024 + lane * 16;
+        const int row = flat / C::RB, chunk = (flat % C::RB) >> 4;
+        if (q_wave0 + row < Nq) *(u32x4_t*)(Oh + (int64_t)(q_wave0 + row) * D + chunk * 8) = z;
+      }
+      if (q_wave0 + l32 < Nq && hh == 0) LSE[(int64_t)bh * Nq + q_wave0 + l32] = -INFINITY;
+      return false;
+    }
+  }
 
   // ---- asynchronous global -> LDS tile loads, issued by the four waves of group 0 inside their
   // MFMA phases (their vector units are idle there).  One instruction moves 16 bytes per lane
@@ -161,7 +208,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // With an even tile count the step past the last tile reloads into kb0; when a next block
   // follows, that load fetches the next block's first K tile instead (it lands in kb0, where the
   // next block expects it), and the next block skips its own first load, wait and barrier.
-  const bool do_pf = has_next && (n % 2 == 0);
+  const bool do_pf = !MASKED && has_next && (n % 2 == 0);
   const uint16_t* nKh = K + (int64_t)nkvh * Nk * D;
   const int nrot = CAUSAL ? 0 : (int)(((int64_t)nqblk * n) / n_qblk);
   auto issue_one = [&](const uint16_t* src, int t, char* buf, int i) {
@@ -206,6 +253,14 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // normalised, see softmax_phase).
   float m2 = -INFINITY, lsum = 0.f, csum = 0.f;
   f32x16_t s0, s1;  // S^T of the current tile, two 32-key blocks
+  // With a mask: the lane's row's 64-bit mask word for the tile whose softmax comes next, loaded
+  // one softmax phase ahead (the one for the first tile before the loop).
+  const uint64_t* mrow = nullptr;
+  uint64_t mword = 0;
+  if constexpr (MASKED) {
+    mrow = mk.words + (int64_t)min(q_wave0 + l32, Nq - 1) * mk.nT;
+    mword = mrow[first_tile];
+  }
   u32x4_t pb[4];    // bf16 P^T of the previous tile, four 16-key groups
 
   // S_j = K_j Q^T
@@ -303,6 +358,21 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // exact.  LSE keeps the fp32 sum l.
   auto softmax_phase = [&](int j) {
     const int tile0 = tile_of(j) * C::BC;
+    uint64_t mcur = 0;
+    if constexpr (MASKED) {
+      mcur = mword;
+      mword = mrow[tile_of(j + 1)];  // the next tile's word (a valid tile's when j + 1 == n)
+      if (partial(j)) {
+        // key 16 (jj / 8) + 8 hh + jj % 8 of the tile is in s0[jj], that key + 32 in s1[jj]
+        const uint32_t lo = (uint32_t)(mcur >> (8 * hh)), hi = (uint32_t)(mcur >> (32 + 8 * hh));
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int b = 16 * (jj >> 3) + (jj & 7);
+          if (!((lo >> b) & 1u)) s0[jj] = -INFINITY;
+          if (!((hi >> b) & 1u)) s1[jj] = -INFINITY;
+        }
+      }
+    }
     if ((tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag)) {
       const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32 + diag) : Nk - 1;  // last key this lane's query sees
 #pragma unroll
@@ -325,14 +395,16 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     }
     if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
       const float mnew = fmaxf(m2, mx);
-      const float alpha = fast_exp2(m2 - mnew);
+      // with a mask a row may still have seen no key (m2 = mnew = -inf): its sums stay 0
+      const float alpha = (MASKED && mnew == -INFINITY) ? 1.f : fast_exp2(m2 - mnew);
       m2 = mnew;
       lsum *= alpha;
       csum *= alpha;
 #pragma unroll
       for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] *= alpha;
     }
-    const float nm = -m2;
+    // a row that has seen no key yet (mask only) has only -inf scores here: exp2(-inf + 0) = 0
+    const float nm = (MASKED && m2 == -INFINITY) ? 0.f : -m2;
     {  // the same FMA and exp2 as that key's own exponential below, so the two round alike
       const float pmax = fast_exp2(__builtin_fmaf(smax, sl2, nm));
       csum += bf16_round(pmax) - pmax;
@@ -354,6 +426,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     // Keep this phase's vector work in this phase: without the fence the compiler sinks the
     // exponentials past the barrier, next to their use in the other group's MFMA phase.
     asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum), "+v"(m2), "+v"(csum));
+    (void)mcur;
   };
 
   // Workgroup barrier between half-periods.  It waits for this wave's LDS reads (the slot may
@@ -449,7 +522,8 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   uint16_t* Oh = O + (int64_t)bh * Nq * D;
   float* Lh = LSE + (int64_t)bh * Nq;
   const float l = sum_across_halves(lsum);
-  const float inv = 1.f / (l + csum);
+  // a row with no visible key (mask only) has l = 0: O = 0, and LSE = -inf below
+  const float inv = (MASKED && !(l + csum > 0.f)) ? 0.f : 1.f / (l + csum);
   const int q = q_wave0 + l32;
   // Lane index behind an empty asm: the staging addresses below are derived from it, so the
   // compiler cannot hoist them into the tile loop, where they would hold registers for nothing.
@@ -490,13 +564,19 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
 // equal anyway).  With xcd_split, the items of XCD x (workgroups b with b % 8 == x) are a
 // contiguous range ordered by head, so the 32 CUs of an XCD work on about two heads at a time and
 // share their K/V in that XCD's L2.  The workgroup walks its blocks as one sequence, so each block
-// can prefetch the next one's Q fragments and first K tile.
-template <int D, bool CAUSAL>
+// can prefetch the next one's Q fragments and first K tile.  With a mask (MASKED) the items are
+// single blocks in order, each walking its own list of non-empty tiles.
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int n_items, int items_per_head,
-    int xcd_split, float sl2, int H, int group, int diag, int paired) {
+    int xcd_split, float sl2, int H, int group, int diag, int paired, const int* __restrict__ mcounts,
+    const uint16_t* __restrict__ mlists, const uint64_t* __restrict__ mwords, int nT) {
   using C = Bf16Cfg<D>;
+  static_assert(!(CAUSAL && MASKED), "a causal mask is one element mask among others");
+  // LDS copy of the current block's tile list (masked forward only)
+  __shared__ uint16_t tl[MASKED ? kMaxMaskTiles : 1];
+  const MaskView mk{mcounts, mlists, mwords, nT, tl};
   // Two-slot rings for K and V tiles.  Separate arrays let the compiler see that reads of one
   // slot never alias the asynchronous loads into another.
   __shared__ __attribute__((aligned(1024))) char kb0[C::TILE_BYTES];
@@ -558,8 +638,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool has_next = it2 < it_end;
     int nbh = bh, nkvh = kvh, nqblk = qblk;
     if (has_next) block_of(it2, k2, nbh, nkvh, nqblk);
-    pre = fwd_block<D, CAUSAL>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, qblk, n_qblk, kb0, kb1, vb0, vb1, stg,
-                               qf.f, pre, has_next, nbh, nkvh, nqblk);
+    pre = fwd_block<D, CAUSAL, MASKED>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, qblk, n_qblk, kb0, kb1, vb0,
+                                       vb1, stg, qf.f, pre, has_next, nbh, nkvh, nqblk, mk);
     it = it2;
     k = k2;
   }
@@ -683,19 +763,20 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED = false>
 hipError_t launch_bf16_impl(const FwdArgs& a, hipStream_t stream) {
   using C = Bf16Cfg<D>;
+  static_assert(C::BR == kFwdBlockRows, "the mask classification works on the forward's query blocks");
   const int n_qblk = (a.Nq + C::BR - 1) / C::BR;
   const int paired = (CAUSAL && (int64_t)a.B * a.H * ((n_qblk + 1) / 2) >= a.num_cus) ? 1 : 0;
   const int items_per_head = paired ? (n_qblk + 1) / 2 : n_qblk;
   const int64_t n_items = (int64_t)a.B * a.H * items_per_head;
   const int64_t grid = n_items < a.num_cus ? n_items : a.num_cus;
   const int xcd_split = (grid % 8 == 0 && n_items % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASKED>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.Nq, a.Nk, n_qblk, (int)n_items, items_per_head, xcd_split, a.scale * kLog2e, a.H,
-                     a.H / a.H_kv, a.diag, paired);
+                     a.H / a.H_kv, a.diag, paired, a.mask_counts, a.mask_lists, a.mask_words, a.mask_tiles);
   return hipGetLastError();
 }
 
@@ -714,6 +795,10 @@ hipError_t launch_f32_impl(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.causal ? launch_bf16_impl<128, true>(a, stream) : launch_bf16_impl<128, false>(a, stream);
   return a.causal ? launch_bf16_impl<64, true>(a, stream) : launch_bf16_impl<64, false>(a, stream);
+}
+
+hipError_t launch_fwd_bf16_masked(const FwdArgs& a, hipStream_t stream) {
+  return a.d == 128 ? launch_bf16_impl<128, false, true>(a, stream) : launch_bf16_impl<64, false, true>(a, stream);
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {

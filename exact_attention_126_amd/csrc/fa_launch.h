@@ -9,6 +9,11 @@ namespace fa {
 
 // Size of the fixed device scratch behind fa_decode_noalloc (its split partials).
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+// Query rows per block of the bf16 forward, the granularity of the mask classification.
+constexpr int kFwdBlockRows = 256;
+// Largest number of 64-key tiles per row the masked forward takes (its block's tile list is held
+// in LDS): Nk <= 131072.
+constexpr int kMaxMaskTiles = 2048;
 
 struct FwdArgs {
   const void* q;
@@ -22,6 +27,19 @@ struct FwdArgs {
   int diag;    // causal: key j visible to query i iff j <= i + diag (0 top-left, Nk - Nq bottom-right)
   float scale;
   int num_cus;  // compute units of the device the stream runs on (persistent grid size)
+  // masked forward only (null / 0 otherwise): per query block of kFwdBlockRows rows the number and
+  // list of non-empty 64-key tiles (bit 15 = partial), and the bit-packed element mask
+  const int* mask_counts = nullptr;
+  const uint16_t* mask_lists = nullptr;
+  const uint64_t* mask_words = nullptr;
+  int mask_tiles = 0;  // 64-key tiles per row, ceil(Nk / 64)
+};
+
+struct MaskClassifyArgs {
+  const uint64_t* mask;  // [Nq][nT] bit-packed element mask
+  int Nq, Nk, nT, br, n_qblk;
+  int* counts;      // [n_qblk]
+  uint16_t* lists;  // [n_qblk][nT]
 };
 
 struct FwdFp8Args {
@@ -93,6 +111,8 @@ struct BwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_mask_classify(const MaskClassifyArgs& a, hipStream_t stream);
+hipError_t launch_fwd_bf16_masked(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_split_bf16(const DecodeSplitArgs& a, hipStream_t stream);
 hipError_t launch_decode_split_f32(const DecodeSplitArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine_bf16(const DecodeCombineArgs& a, hipStream_t stream);

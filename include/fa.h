@@ -55,7 +55,8 @@ typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_CAUSAL_BOTTOM_RIGHT
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
-  FA_ERR_ALIGN = 2,       /* q/k/v/o/workspace not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_ALIGN = 2,       /* q/k/v/o/workspace not 16-byte aligned, lse not 4-byte aligned, or the
+                             mask of fa_fwd_masked not 8-byte aligned */
   FA_ERR_SHAPE = 3,       /* a size <= 0, H_kv not dividing H, causal with Nq != Nk (fa_fwd) or
                              bottom-right with Nk < Nq, or sizes beyond the index limits */
   FA_ERR_UNSUPPORTED = 4, /* d not in {64, 128}, unknown dtype, or fp32 in the backward */
@@ -110,6 +111,29 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, const float*
                        const float* k_scale, const float* v_scale, void* o, float* lse, int64_t B,
                        int64_t H, int64_t H_kv, int64_t Nq, int64_t Nk, int64_t d, fa_mask_t mask,
                        float scale, hipStream_t stream);
+
+/*
+ * Forward with an arbitrary element mask (the Day-21 page's §6 table, last row: blocks the mask
+ * leaves empty are skipped, partly visible blocks are masked element by element; the Q31 answer
+ * "FlashAttention 为什么快", §2, names arbitrary masks as what FlashAttention-2 lacks).
+ *   q [B,H,Nq,d], k and v [B,H_kv,Nk,d] bf16 (in); o [B,H,Nq,d] bf16 and lse [B,H,Nq] float32
+ *   (out), as fa_fwd_ex with no mask except that key j is visible to query row i iff bit (j % 64)
+ *   of mask[i * ceil(Nk/64) + j / 64] is 1.  The mask is one [Nq][ceil(Nk/64)] array of 64-bit
+ *   words in device memory, shared by every batch and head; bits of keys >= Nk are ignored.  A row
+ *   with no visible key gets O = 0 and LSE = -inf.
+ *   workspace: caller-owned device memory of at least fa_fwd_masked_workspace_bytes(Nq, Nk)
+ *   bytes, 16-byte aligned.  A first kernel classifies every (block of 256 query rows, 64-key
+ *   tile) of the mask as empty, full or partial and writes each block's list of non-empty tiles
+ *   there; the forward then streams only those tiles and applies the element mask only on the
+ *   partial ones.  The workspace holds nothing across calls.
+ *   dtype must be FA_DTYPE_BF16; d 64 or 128; Nk <= 131072 (FA_ERR_SHAPE beyond); mask 8-byte
+ *   aligned.  Other limits and errors as for fa_fwd_ex.
+ */
+size_t fa_fwd_masked_workspace_bytes(int64_t Nq, int64_t Nk);
+fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t Nq, int64_t Nk, int64_t d,
+                          const uint64_t* mask, void* workspace, size_t workspace_bytes, float scale,
+                          fa_dtype_t dtype, hipStream_t stream);
 
 /*
  * Split-KV decode (one query token per (b, h) against a KV cache): the keys are split into

@@ -16,6 +16,12 @@ M4-047 card §3):
 Rows may be processed in chunks to bound memory, but every chunk spans all keys,
 so each row's two passes see the whole row.  Nothing here uses the online recurrence.
 
+Arbitrary masks (the "skip masked blocks, mask partial ones element by element" rule of the
+Day-21 page's §6 table, and the arbitrary masks FlashAttention-2 is said to lack in the Q31
+answer §2): an element mask `allowed` [Nq, Nk] of booleans, key j visible to query row i iff
+allowed[i, j]; S_ij = -inf where it is not.  A row with no visible key has an empty softmax:
+its O row is 0 (a sum over no keys) and its LSE is ln 0 = -inf.
+
 Grouped K/V heads (GQA: several query heads share one K/V head; the Day-21 page's FAQ Q5 lists
 it among the techniques that matter at decode, where reading the KV cache is the bottleneck):
 with H query heads and H_kv K/V heads, H_kv dividing H, query head h reads K/V head
@@ -54,12 +60,13 @@ def softmax_two_pass(s: np.ndarray):
 
 
 def attention_head(q, k, v, scale: float, causal: bool = False, rows=None, row_chunk: int = 1024,
-                   diag: int = 0):
+                   diag: int = 0, allowed=None):
     """One head. q [Nq, d], k and v [Nk, d] -> (O [n, d], LSE [n]) in float64.
 
-    rows: optional increasing 1-D array of query row indices to compute (the causal
-    mask uses the true row index); default all rows.  causal: key j is visible to query
-    row i iff j <= i + diag.
+    rows: optional increasing 1-D array of query row indices to compute (the masks use the
+    true row index); default all rows.  causal: key j is visible to query row i iff
+    j <= i + diag.  allowed: optional boolean element mask [Nq, Nk] (key j visible to row i iff
+    allowed[i, j]); a row it leaves without keys gets O = 0 and LSE = -inf.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
@@ -70,16 +77,24 @@ def attention_head(q, k, v, scale: float, causal: bool = False, rows=None, row_c
         s = float(scale) * (q[r] @ k.T)
         if causal:
             s = np.where(np.arange(k.shape[0])[None, :] > r[:, None] + diag, -np.inf, s)
+        if allowed is not None:
+            s = np.where(np.asarray(allowed, dtype=bool)[r], s, -np.inf)
+            empty = np.isneginf(s).all(axis=1)
+            s[empty] = 0.0  # placeholder scores for rows without keys; their results are set below
         p, m, l = softmax_two_pass(s)
         o[c0:c0 + len(r)] = p @ v
         lse[c0:c0 + len(r)] = m + np.log(l)
+        if allowed is not None:
+            o[c0:c0 + len(r)][empty] = 0.0
+            lse[c0:c0 + len(r)][empty] = -np.inf
     return o, lse
 
 
-def attention(q, k, v, scale: float, causal: bool = False, row_chunk: int = 1024, diag: int = 0):
+def attention(q, k, v, scale: float, causal: bool = False, row_chunk: int = 1024, diag: int = 0, allowed=None):
     """[B, H, Nq, d] x [B, H_kv, Nk, d] x [B, H_kv, Nk, d] -> (O [B, H, Nq, d], LSE [B, H, Nq]) float64.
 
-    H_kv must divide H; query head h attends with K/V head h // (H // H_kv)."""
+    H_kv must divide H; query head h attends with K/V head h // (H // H_kv).  allowed: one
+    element mask [Nq, Nk] for every batch and head (see attention_head)."""
     q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     B, H, Nq, _ = q.shape
     H_kv = k.shape[1]
@@ -91,7 +106,7 @@ def attention(q, k, v, scale: float, causal: bool = False, row_chunk: int = 1024
     for b in range(B):
         for h in range(H):
             o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h // group], v[b, h // group], scale, causal,
-                                                row_chunk=row_chunk, diag=diag)
+                                                row_chunk=row_chunk, diag=diag, allowed=allowed)
     return o, lse
 
 

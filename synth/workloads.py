@@ -41,6 +41,10 @@ class Workload:
     #                     (batch, K/V head)
     q_dtype: str = ""  # "" (as dtype) or "e4m3": Q stored as E4M3 codes with a scale per (batch, head)
     causal_align: str = "top_left"  # or "bottom_right": key j visible to row i iff j <= i + Nk - Nq
+    # Element mask (synth.masks): () none, ("documents", seed, min_len, max_len) packed documents
+    # with causal attention inside each, ("window", w) a causal sliding window of w keys,
+    # ("tiles", seed, bq, bk) random empty / full / bit-by-bit tiles of bq x bk elements
+    mask_rule: tuple = ()
 
     @property
     def kv_heads(self) -> int:
@@ -98,6 +102,11 @@ WORKLOADS = {
             causal=False, seed=8000, num_splits=64,
             description="1-token decode against an FP8 (E4M3) KV cache with a scale per (batch, head), "
                         "64-way split-KV + combine"),
+        Workload(
+            "masked_docs_b4h16_n8192_d128", B=4, H=16, Nq=8192, Nk=8192, d=128, dtype="bf16", causal=False,
+            seed=10000, mask_rule=("documents", 10001, 256, 3072),
+            description="8192 tokens packed from documents of 256 to 3072 tokens (seeded lengths), each token "
+                        "attending causally within its own document; one element mask for every batch and head"),
         Workload(
             "prefill_fp8_b8h16_n8192_d128_causal", B=8, H=16, Nq=8192, Nk=8192, d=128, dtype="bf16",
             kv_dtype="e4m3", q_dtype="e4m3", causal=True, seed=9000, k_rule=("scale_all", 2.0),

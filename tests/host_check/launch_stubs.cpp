@@ -16,4 +16,6 @@ hipError_t launch_bwd_bf16(const BwdArgs&, hipStream_t) { return hipErrorNoDevic
 hipError_t launch_decode_split_fp8kv(const DecodeSplitFp8Args&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_fwd_fp8(const FwdFp8Args&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t decode_scratch_address(void**) { return hipErrorNoDevice; }
+hipError_t launch_mask_classify(const MaskClassifyArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_fwd_bf16_masked(const FwdArgs&, hipStream_t) { return hipErrorNoDevice; }
 }  // namespace fa

@@ -47,6 +47,21 @@ def pool():
     return _POOL
 
 
+_MASK = {}
+
+
+def _allowed(w):
+    """The workload's element mask (None without one), built once per worker."""
+    if not w.mask_rule:
+        return None
+    key = (w.Nq, w.Nk, w.mask_rule)
+    if key not in _MASK:
+        from synth import masks
+        _MASK.clear()
+        _MASK[key] = masks.element_mask(w)
+    return _MASK[key]
+
+
 def _head_job(args):
     """(w, b, h) -> (b, h, O [Nq, d], LSE [Nq]) float64 from the reference on regenerated inputs."""
     import oracle
@@ -56,7 +71,7 @@ def _head_job(args):
     q = si.head_block_f32(w, "q", b, h)
     k = si.head_block_f32(w, "k", b, hk)
     v = si.head_block_f32(w, "v", b, hk)
-    o, lse = oracle.attention_head(q, k, v, w.scale, w.causal, diag=w.diag)
+    o, lse = oracle.attention_head(q, k, v, w.scale, w.causal, diag=w.diag, allowed=_allowed(w))
     return b, h, o, lse
 
 

@@ -221,6 +221,27 @@ def test_decode_noalloc_validation(L):
     assert noalloc(L, B=1024, H=64, H_kv=8, Nk=32768, d=128, S=64) == 8
 
 
+def masked(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=4, H_kv=2, Nq=300, Nk=500, d=128, mask=P, ws=P, wsb=1 << 20,
+           scale=0.125, dtype=BF16):
+    vp = ctypes.c_void_p
+    return L.fa_fwd_masked(vp(q) if q else None, vp(k) if k else None, vp(v) if v else None, vp(o) if o else None,
+                           vp(lse) if lse else None, B, H, H_kv, Nq, Nk, d, vp(mask) if mask else None,
+                           vp(ws) if ws else None, wsb, scale, dtype, None)
+
+
+def test_fwd_masked_validation(L):
+    # two 256-row blocks of 8 tiles: 16 bytes of counts (two, padded), then 2 x 8 list entries
+    assert fa.fa_fwd_masked_workspace_bytes(300, 500) == 16 + 2 * 2 * 8
+    assert fa.fa_fwd_masked_workspace_bytes(0, 500) == 0 and fa.fa_fwd_masked_workspace_bytes(10, 131073) == 0
+    assert masked(L, mask=0) == 1 and masked(L, ws=0) == 1 and masked(L, q=0) == 1
+    assert masked(L, dtype=F32) == 4 and masked(L, d=96) == 4
+    assert masked(L, mask=P + 4) == 2 and masked(L, ws=P + 8) == 2 and masked(L, o=P + 8) == 2
+    assert masked(L, mask=P + 8) in (0, 6)  # 8-byte aligned mask words are enough
+    assert masked(L, H_kv=3) == 3 and masked(L, Nq=0) == 3 and masked(L, Nk=131073) == 3
+    assert masked(L, scale=float("inf")) == 7
+    assert masked(L, wsb=fa.fa_fwd_masked_workspace_bytes(300, 500) - 1) == 5
+
+
 def test_binding_combine_checks_output_shapes():
     """The combine writes B*H LSE values and B*H*d outputs, with B, H and d taken from o: a short
     lse or an o that is not [B,H,1,d] is rejected before the library is called."""
