@@ -602,15 +602,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   }
   const int g = blockIdx.x;
-  int it = g, it_end = n_items, stride = gridDim.x;
-  if (xcd_split) {
+  int it0 = g, it_end = n_items, stride = gridDim.x;
+  if (!MASKED && xcd_split) {
     const int per = n_items >> 3;
-    it = (g & 7) * per + (g >> 3);
+    it0 = (g & 7) * per + (g >> 3);
     it_end = (g & 7) * per + per;
     stride = gridDim.x >> 3;
   }
+  // Item of this workgroup's step r.  With a mask the items are (query block, head) in block-major
+  // order and workgroup g takes position g of every even round of gridDim.x items and position
+  // gridDim.x - 1 - g of every odd one: the blocks' tile counts differ and every workgroup sees
+  // a different block in each round, so the sums even out.
+  auto item_at = [&](int r) {
+    if constexpr (MASKED) return r * (int)gridDim.x + ((r & 1) ? (int)gridDim.x - 1 - g : g);
+    else return it0 + r * stride;
+  };
   // Block k of item it: its head, K/V head and query block, and the number of blocks of the item.
   auto block_of = [&](int item, int k, int& bh, int& kvh, int& qblk) {
+    if constexpr (MASKED) {
+      const int nbh_all = n_items / n_qblk;
+      bh = item % nbh_all;
+      qblk = item / nbh_all;
+      kvh = (bh / H) * (H / group) + (bh % H) / group;
+      return 1;
+    }
     bh = item / items_per_head;
     const int r = item % items_per_head;
     kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
@@ -620,27 +635,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   typename Bf16Cfg<D>::QFrag qf;
   bool pre = false;
-  int k = 0;
-  if (it < it_end) {
+  int r = 0, k = 0;
+  if (item_at(0) < it_end) {
     int bh, kvh, qblk;
-    block_of(it, 0, bh, kvh, qblk);
+    block_of(item_at(0), 0, bh, kvh, qblk);
     load_q_frags<D>(qf.f, Q, bh, Nq, qblk * Bf16Cfg<D>::BR + (threadIdx.x >> 6) * 32, threadIdx.x & 31,
                     (threadIdx.x >> 5) & 1);
   }
-  while (it < it_end) {
+  while (item_at(r) < it_end) {
     int bh, kvh, qblk;
-    const int cnt = block_of(it, k, bh, kvh, qblk);
-    int it2 = it, k2 = k + 1;
+    const int cnt = block_of(item_at(r), k, bh, kvh, qblk);
+    int r2 = r, k2 = k + 1;
     if (k2 >= cnt) {
-      it2 += stride;
+      r2 = r + 1;
       k2 = 0;
     }
-    const bool has_next = it2 < it_end;
+    const bool has_next = item_at(r2) < it_end;
     int nbh = bh, nkvh = kvh, nqblk = qblk;
-    if (has_next) block_of(it2, k2, nbh, nkvh, nqblk);
+    if (has_next) block_of(item_at(r2), k2, nbh, nkvh, nqblk);
     pre = fwd_block<D, CAUSAL, MASKED>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, qblk, n_qblk, kb0, kb1, vb0,
                                        vb1, stg, qf.f, pre, has_next, nbh, nkvh, nqblk, mk);
-    it = it2;
+    r = r2;
     k = k2;
   }
 }
@@ -772,7 +787,7 @@ hipError_t launch_bf16_impl(const FwdArgs& a, hipStream_t stream) {
   const int items_per_head = paired ? (n_qblk + 1) / 2 : n_qblk;
   const int64_t n_items = (int64_t)a.B * a.H * items_per_head;
   const int64_t grid = n_items < a.num_cus ? n_items : a.num_cus;
-  const int xcd_split = (grid % 8 == 0 && n_items % 8 == 0) ? 1 : 0;
+  const int xcd_split = (!MASKED && grid % 8 == 0 && n_items % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASKED>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.Nq, a.Nk, n_qblk, (int)n_items, items_per_head, xcd_split, a.scale * kLog2e, a.H,

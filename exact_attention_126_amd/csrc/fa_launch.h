@@ -38,6 +38,7 @@ struct FwdArgs {
 struct MaskClassifyArgs {
   const uint64_t* mask;  // [Nq][nT] bit-packed element mask
   int Nq, Nk, nT, br, n_qblk;
+  uint8_t* cls;     // [n_qblk][nT] class of each tile: 0 empty, 1 full, 2 partial
   int* counts;      // [n_qblk]
   uint16_t* lists;  // [n_qblk][nT]
 };

@@ -230,8 +230,9 @@ def masked(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=4, H_kv=2, Nq=300, Nk=500, d=128
 
 
 def test_fwd_masked_validation(L):
-    # two 256-row blocks of 8 tiles: 16 bytes of counts (two, padded), then 2 x 8 list entries
-    assert fa.fa_fwd_masked_workspace_bytes(300, 500) == 16 + 2 * 2 * 8
+    # two 256-row blocks of 8 tiles: counts (2 x 4 bytes, padded to 16), classes (2 x 8 bytes), lists
+    # (2 x 8 x 2 bytes)
+    assert fa.fa_fwd_masked_workspace_bytes(300, 500) == 16 + 16 + 2 * 8 * 2
     assert fa.fa_fwd_masked_workspace_bytes(0, 500) == 0 and fa.fa_fwd_masked_workspace_bytes(10, 131073) == 0
     assert masked(L, mask=0) == 1 and masked(L, ws=0) == 1 and masked(L, q=0) == 1
     assert masked(L, dtype=F32) == 4 and masked(L, d=96) == 4

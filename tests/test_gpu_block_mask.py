@@ -44,6 +44,10 @@ SMALL = [
     _w("window1_n200_d64", 1, 2, 2, 200, 200, 64, ("window", 1)),
     _w("docs_n1000_d64", 1, 3, 3, 1000, 1000, 64, ("documents", 5, 40, 400)),
     _w("tiles_nq1_nk500", 1, 2, 2, 1, 500, 128, ("tiles", 6, 1, 64)),
+    # more (block, head) items than compute units, a multiple of 8: every workgroup walks several
+    # blocks of different tile counts in sequence
+    _w("docs_b2h64_n2048_seq", 2, 64, 16, 2048, 2048, 64, ("documents", 8, 100, 900)),
+    _w("tiles_b4h40_n1300_seq", 4, 40, 40, 1300, 1300, 128, ("tiles", 9, 96, 80)),
 ]
 
 
@@ -141,8 +145,10 @@ def test_tile_classification_exact(w):
     _, _, ws = _run(w, dev, allowed)
     n_qblk, nt = -(-w.Nq // 256), -(-w.Nk // 64)
     raw = ws.cpu().numpy()
+    off_cls = (4 * n_qblk + 15) // 16 * 16
+    off_lst = off_cls + (n_qblk * nt + 15) // 16 * 16
     counts = raw[:4 * n_qblk].view(np.int32)
-    lists = raw[(4 * n_qblk + 15) // 16 * 16:][:2 * n_qblk * nt].view(np.uint16).reshape(n_qblk, nt)
+    lists = raw[off_lst:off_lst + 2 * n_qblk * nt].view(np.uint16).reshape(n_qblk, nt)
     hc, hl = _host_classification(allowed, w.Nq, w.Nk)
     assert counts.tolist() == hc
     for qb in range(n_qblk):
