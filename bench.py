@@ -256,6 +256,15 @@ def time_extras(torch, fa, si, get, reps: int = 20) -> dict:
         out[name] = {"workload": w.name, "entry": "fa_fwd (" + ("fp32" if w.dtype == "f32" else "bf16") +
                      (", causal)" if w.causal else ")"), "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
                      "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+        if w.d == 64 and w.dtype == "bf16":
+            # d = 64: an MFMA phase is 16 MFMAs (512 cycles per 64-key tile) while the softmax of the tile is
+            # about 154 VALU instructions per wave (counted, profiles/counters_fwd_valu_issue_*), 616 cycles at
+            # one wave64 instruction per 4 cycles: the VALU issue roof is 512 / 616 of the matrix-core peak
+            valu_roof = PEAK_BF16_TFLOPS * 512 / (154 * 4)
+            out[name]["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                     "valu_issue_roof": round(valu_roof, 1),
+                                     "frac_of_valu_issue_roof": round(tf / valu_roof, 4)}
         del dev, o, lse
     w = get("chunk_prefill_b1h32kv8_nq2048_nk16384_d128")
     dev = {x: to_device(w, si.make_tensor(w, x)) for x in "qkv"}
@@ -365,6 +374,10 @@ def main():
                     help="after the timed steps, measure the sustained bf16 MFMA rate (libfa_calib.so)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference point for HBM counters)")
+    ap.add_argument("--kernel-only", metavar="WORKLOAD[:bwd]", default=None,
+                    help="for profiler runs: launch fa_fwd on one forward workload --warmup + --steps times (with "
+                         "':bwd', fa_fwd once and then fa_bwd that many times) and exit, with no timing and no "
+                         "JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards over "
@@ -374,6 +387,31 @@ def main():
 
     from synth import inputs as si
     from synth.workloads import get
+
+    if args.kernel_only:
+        import torch
+        import exact_attention_126_amd as fa
+        name, _, what = args.kernel_only.partition(":")
+        w = get(name)
+        if w.is_decode or w.q_dtype or w.kv_dtype or w.mask_rule or w.kv_heads != w.H or w.causal_align != "top_left":
+            sys.exit(f"--kernel-only takes a plain forward workload (fa_fwd), not {w.name}")
+        if w.dtype == "f32":
+            dev = {x: torch.from_numpy(si.make_tensor(w, x)).cuda() for x in "qkv"}
+        else:
+            dev = {x: to_device(w, si.make_tensor(w, x)) for x in "qkv"}
+        o = torch.empty_like(dev["q"])
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+        if what == "bwd":
+            fa.fa_fwd(dev["q"], dev["k"], dev["v"], o, lse, causal=w.causal, scale=w.scale)
+            do = to_device(w, si.make_tensor(w, "do"))
+            for _ in range(args.warmup + args.steps):
+                fa.attention_backward(dev["q"], dev["k"], dev["v"], o, lse, do, causal=w.causal, scale=w.scale)
+        else:
+            for _ in range(args.warmup + args.steps):
+                fa.fa_fwd(dev["q"], dev["k"], dev["v"], o, lse, causal=w.causal, scale=w.scale)
+        torch.cuda.synchronize()
+        print(f"[bench] --kernel-only {args.kernel_only}: {args.warmup + args.steps} launches", file=sys.stderr)
+        return
 
     cpu_pre = cpu_dec = None
     if args.cpu_baseline == "on":

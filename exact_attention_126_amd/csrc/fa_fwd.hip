@@ -289,6 +289,30 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
         oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[t]), oacc[mb], 0, 0, 0);
       }
   };
+  // At D = 64 (EARLY_MAX) the tile's largest raw score of this lane's row, for tiles that need no
+  // element mask, is taken in the MFMA phase that computes S, under its P V products: its sixteen
+  // dependent max3 steps and the swap across the lane halves.  One wave issues a VALU instruction
+  // only every few cycles, and at D = 64 the softmax phase is twice as long as the MFMA phase, so
+  // moving the steps shortens every half-period (+3%).  At D = 128 the two phases are nearly equal
+  // and the extra VALU work beside the MFMAs costs more than it saves (-0.5 to -1.7%, measured):
+  // the max stays in the softmax phase.
+  constexpr bool EARLY_MAX = (D == 64);
+  float smax_pre = 0.f, mxp = 0.f;
+  auto max_step = [&](auto St) {  // step St of the max chain over s0, s1
+    constexpr int st = decltype(St)::value;
+    if constexpr (st == 0) mxp = max3f(s0[0], s0[1], s1[0]);
+    else if constexpr (st == 1) mxp = max3f(mxp, s1[1], s0[2]);
+    else if constexpr (st < 15) mxp = max3f(mxp, s1[st], s0[st + 1]);
+    else mxp = max3f(mxp, s1[15], s1[15]);
+  };
+  auto max_halves = [&](float x) {  // across the two lane halves, without fmaxf's canonicalising
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  auto row_max_now = [&]() {
+    static_for<16>([&](auto St) { max_step(St); });
+    smax_pre = max_halves(mxp);
+  };
   // Pins the MFMA results to the phase that computes them (see the fence in softmax_phase).
   auto fence_acc = [&]() {
     asm volatile("" : "+v"(s0), "+v"(s1));
@@ -334,6 +358,16 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
         oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % (L + 1)], as_bf16x8(pb[t]), oacc[mb], 0, 0, 0);
       }
       if constexpr (i + L < N) read(std::integral_constant<int, i + L>{});
+      // the max chain over this phase's S, from the second P V slot on (S is complete by then)
+      constexpr int SPS = (16 + (NP - 3)) / (NP - 2);  // steps per slot over slots NS + 1 .. N - 2
+      if constexpr (EARLY_MAX && i >= NS + 1 && i <= N - 2) {
+        constexpr int k0 = (i - NS - 1) * SPS;
+        static_for<SPS>([&](auto T) {
+          constexpr int st = k0 + decltype(T)::value;
+          if constexpr (st < 16) max_step(std::integral_constant<int, st>{});
+        });
+      }
+      if constexpr (EARLY_MAX && i == N - 1) smax_pre = max_halves(mxp);
       if constexpr (NDMA > 0 && i % DMA_EVERY == 0 && i / DMA_EVERY < NDMA) {
         constexpr int d = i / DMA_EVERY;
         if constexpr (d < C::DMA_PER_WAVE)
@@ -344,6 +378,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
       __builtin_amdgcn_sched_barrier(0);
     });
     fence_acc();
+    if constexpr (EARLY_MAX) asm volatile("" : "+v"(smax_pre));
   };
 
   // Softmax phase j: element mask where the tile reaches past the wave's diagonal or the end of
@@ -359,40 +394,41 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   auto softmax_phase = [&](int j) {
     const int tile0 = tile_of(j) * C::BC;
     uint64_t mcur = 0;
+    const bool cut = (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag);
+    bool edge = cut;
     if constexpr (MASKED) {
       mcur = mword;
       mword = mrow[tile_of(j + 1)];  // the next tile's word (a valid tile's when j + 1 == n)
-      if (partial(j)) {
-        // key 16 (jj / 8) + 8 hh + jj % 8 of the tile is in s0[jj], that key + 32 in s1[jj]
-        const uint32_t lo = (uint32_t)(mcur >> (8 * hh)), hi = (uint32_t)(mcur >> (32 + 8 * hh));
+      edge = edge || partial(j);
+    }
+    if (edge) {
+      if constexpr (MASKED) {
+        if (partial(j)) {
+          // key 16 (jj / 8) + 8 hh + jj % 8 of the tile is in s0[jj], that key + 32 in s1[jj]
+          const uint32_t lo = (uint32_t)(mcur >> (8 * hh)), hi = (uint32_t)(mcur >> (32 + 8 * hh));
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int b = 16 * (jj >> 3) + (jj & 7);
+            if (!((lo >> b) & 1u)) s0[jj] = -INFINITY;
+            if (!((hi >> b) & 1u)) s1[jj] = -INFINITY;
+          }
+        }
+      }
+      if (cut) {
+        const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32 + diag) : Nk - 1;  // last key this lane's query sees
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          const int b = 16 * (jj >> 3) + (jj & 7);
-          if (!((lo >> b) & 1u)) s0[jj] = -INFINITY;
-          if (!((hi >> b) & 1u)) s1[jj] = -INFINITY;
+          const int key = tile0 + 16 * (jj >> 3) + 8 * hh + (jj & 7);
+          if (key > lim) s0[jj] = -INFINITY;
+          if (key + 32 > lim) s1[jj] = -INFINITY;
         }
       }
     }
-    if ((tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag)) {
-      const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32 + diag) : Nk - 1;  // last key this lane's query sees
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int key = tile0 + 16 * (jj >> 3) + 8 * hh + (jj & 7);
-        if (key > lim) s0[jj] = -INFINITY;
-        if (key + 32 > lim) s1[jj] = -INFINITY;
-      }
-    }
-    float mx = max3f(s0[0], s0[1], s1[0]);
-    mx = max3f(mx, s1[1], s0[2]);
-#pragma unroll
-    for (int jj = 2; jj < 15; ++jj) mx = max3f(mx, s1[jj], s0[jj + 1]);
-    mx = max3f(mx, s1[15], s1[15]);
-    float smax;  // the row's largest score in this tile, unscaled
-    {  // across the two lane halves, without fmaxf's canonicalising of the swapped values
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      smax = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
-      mx = smax * sl2;
-    }
+    // the row's largest score in this tile, unscaled (already taken in the MFMA phase when
+    // EARLY_MAX and no element was masked)
+    if (!EARLY_MAX || edge) row_max_now();
+    const float smax = smax_pre;
+    float mx = smax * sl2;
     if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
       const float mnew = fmaxf(m2, mx);
       // with a mask a row may still have seen no key (m2 = mnew = -inf): its sums stay 0
@@ -456,6 +492,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     issue(Vh, 0, vb0);
     qk(kb0);
     fence_acc();
+    if constexpr (EARLY_MAX) row_max_now();
     bar();
     int j = 1;
     for (; j + 1 < n; j += 2) {
@@ -489,6 +526,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     bar();  // h = 0: idle
     qk(kb0);  // h = 1
     fence_acc();
+    if constexpr (EARLY_MAX) row_max_now();
     bar();
     int j = 1;
     for (; j + 1 < n; j += 2) {
