@@ -203,6 +203,27 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
 #pragma unroll
     for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] = mfma8(vfrag(vt, mb), pb, oacc[mb]);
   };
+  // The tile's largest raw score of this lane's row is taken in the MFMA phase that computes S,
+  // under its P V products (sixteen dependent max3 steps, then the swap across the lane halves):
+  // the FP8 MFMA phase is half as long as the softmax phase, whose single wave issues a VALU
+  // instruction only every few cycles.  Tiles that need an element mask take it again after
+  // masking.
+  float smax_pre = 0.f, mxp = 0.f;
+  auto max_step = [&](auto St) {  // step St of the max chain over s0, s1
+    constexpr int st = decltype(St)::value;
+    if constexpr (st == 0) mxp = max3f(s0[0], s0[1], s1[0]);
+    else if constexpr (st == 1) mxp = max3f(mxp, s1[1], s0[2]);
+    else if constexpr (st < 15) mxp = max3f(mxp, s1[st], s0[st + 1]);
+    else mxp = max3f(mxp, s1[15], s1[15]);
+  };
+  auto max_halves = [&](float x) {  // across the two lane halves, without fmaxf's canonicalising
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  auto row_max_now = [&]() {
+    static_for<16>([&](auto St) { max_step(St); });
+    smax_pre = max_halves(mxp);
+  };
   auto fence_acc = [&]() {
     asm volatile("" : "+v"(s0), "+v"(s1));
 #pragma unroll
@@ -237,6 +258,16 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
         oacc[i - NS] = mfma8(frag[i % (L + 1)], pb, oacc[i - NS]);
       }
       if constexpr (i + L < N) read(std::integral_constant<int, i + L>{});
+      // the max chain over this phase's S, from the second P V slot on (S is complete by then)
+      constexpr int SPS = (16 + (NP - 2)) / (NP - 1);  // steps per slot over slots NS + 1 .. N - 1
+      if constexpr (i >= NS + 1) {
+        constexpr int k0 = (i - NS - 1) * SPS;
+        static_for<SPS>([&](auto T) {
+          constexpr int st = k0 + decltype(T)::value;
+          if constexpr (st < 16) max_step(std::integral_constant<int, st>{});
+        });
+      }
+      if constexpr (i == N - 1) smax_pre = max_halves(mxp);
       if constexpr (NDMA > 0 && i % DMA_EVERY == 0 && i / DMA_EVERY < NDMA) {
         constexpr int d = i / DMA_EVERY;
         if constexpr (d < C::DMA_PER_WAVE)
@@ -247,6 +278,7 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
       __builtin_amdgcn_sched_barrier(0);
     });
     fence_acc();
+    asm volatile("" : "+v"(smax_pre));
   };
 
   // Softmax phase j: mask, lazy max, P_j = exp2(S_j * sl2 - m + kBias) rounded to E4M3, row sums.
@@ -260,16 +292,9 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
         if (key > lim) s0[jj] = -INFINITY;
         if (key + 32 > lim) s1[jj] = -INFINITY;
       }
+      row_max_now();
     }
-    float mx = max3f(s0[0], s0[1], s1[0]);
-    mx = max3f(mx, s1[1], s0[2]);
-#pragma unroll
-    for (int jj = 2; jj < 15; ++jj) mx = max3f(mx, s1[jj], s0[jj + 1]);
-    mx = max3f(mx, s1[15], s1[15]);
-    {  // across the two lane halves, without fmaxf's canonicalising of the swapped values
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1])) * sl2;
-    }
+    const float mx = smax_pre * sl2;
     if (__builtin_amdgcn_ballot_w64(mx > m2 + kTau) != 0) {
       const float mnew = fmaxf(m2, mx);
       const float alpha = fast_exp2(m2 - mnew);
@@ -316,6 +341,7 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
     issue(Vh, 0, vb0);
     qk(kb0);
     fence_acc();
+    row_max_now();
     bar();
     int j = 1;
     for (; j + 1 < n; j += 2) {
@@ -348,6 +374,7 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
     bar();
     qk(kb0);
     fence_acc();
+    row_max_now();
     bar();
     int j = 1;
     for (; j + 1 < n; j += 2) {
