@@ -14,12 +14,13 @@
 //    v_mfma_f32_32x32x16_bf16 with Q^T and dO^T held in VGPRs, then dS^T in VGPRs, then
 //    dQ^T += K^T dS^T with K^T read from LDS by the transposing ds_read_b64_tr_b16.  The
 //    accumulator-to-B-operand key order (key_of_row) is the forward's.
-//  * bwd_dkdv_kernel: key-major.  Each wave owns 16 keys, with their K and V fragments in VGPRs,
-//    and streams 32-query tiles of Q, dO, LSE and Dr through LDS: S = Q K^T and dP = dO V^T on
-//    v_mfma_f32_16x16x32_bf16, then P and dS, then dV^T += dO^T P and dK^T += Q^T dS.  Query
-//    rows are loaded in the order that makes the 16x16 accumulators directly the B operands of
-//    the last two products.  With grouped K/V heads the workgroup loops over the query heads that
-//    share its K/V head and its dK, dV sum over them.
+//  * bwd_dkdv_kernel: key-major, the mirror image of bwd_dq_kernel.  Each wave (one per SIMD)
+//    owns 32 keys, with their K^T and V^T fragments in VGPRs, and streams 32-query tiles of Q,
+//    dO, LSE and Dr through LDS: S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16_bf16, then P
+//    and dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read by the transposing
+//    ds_read_b64_tr_b16.  Query rows are loaded in the key_of_row order, so the accumulators are
+//    directly the B operands of the last two products.  With grouped K/V heads the workgroup
+//    loops over the query heads that share its K/V head and its dK, dV sum over them.
 // Recomputing S and dP in both big kernels costs 7 matrix products instead of 5, and keeps both
 // free of the cross-workgroup dQ reduction a single kernel would need.
 #include "fa_device.h"
@@ -28,8 +29,6 @@
 
 namespace fa {
 namespace {
-
-typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
 // Work item of this workgroup.  Consecutive workgroups go to the eight XCDs in turn; remapping
 // them so that XCD x runs the contiguous item range x * n / 8 .. keeps the items of one head on
@@ -245,264 +244,359 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ------------------------------------------------------------------ dK, dV
 #ifndef FA_BWD_LOOKAHEAD
-#define FA_BWD_LOOKAHEAD 7  // MFMAs by which the dK/dV kernel's LDS operand reads run ahead
+#define FA_BWD_LOOKAHEAD 3  // MFMAs by which the dK/dV kernel's LDS operand reads run ahead
 #endif
 
+// Key-major, one wave per SIMD: each wave owns 32 keys, so that every 16-byte LDS operand read
+// feeds a 32x32x16 MFMA (32 keys x 32 queries x 16) and the Q and dO tiles, read twice per wave
+// (as rows for S and dP, transposed for dK and dV), cost one LDS byte per 32 FLOP.  The 32-key
+// accumulators of dK^T and dV^T with the K and V fragments take more registers than two waves
+// per SIMD have, so the wave overlaps its own work: while the matrix core computes S and dP of
+// the next query tile, the VALU turns the current tile's S and dP into P and dS.
 template <int D>
 struct DkvCfg {
-  static constexpr int WAVES = 8;
+  static constexpr int WAVES = 4;        // one per SIMD
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int BK = WAVES * 16;  // keys per workgroup
+  static constexpr int BK = WAVES * 32;  // keys per workgroup, 32 per wave
   static constexpr int BQ = 32;          // queries per tile
-  static constexpr int RB = D * 2;
-  static constexpr int CPR = D / 8;
+  static constexpr int SLOTS = 3;        // LDS ring: the tile in use, the next, one loading
+  static constexpr int RB = D * 2;       // bytes per LDS row
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int TILE_BYTES = BQ * RB;
   static constexpr int ROWS_PER_DMA = 64 / CPR;
-  static constexpr int DMAS = TILE_BYTES / 1024;                       // per tensor and tile
-  static constexpr int DMA_PER_WAVE = (2 * DMAS + WAVES - 1) / WAVES;  // Q and dO together
-  static constexpr int KS = D / 32;                                    // k-steps of S = Q K^T
-  static constexpr int DB = D / 16;                                    // 16-dim blocks of dK^T, dV^T
+  static constexpr int DMAS = TILE_BYTES / 1024;         // per tensor and tile
+  static constexpr int DMA_PER_WAVE = 2 * DMAS / WAVES;  // Q and dO together
+  static constexpr int KSTEPS = D / 16;                  // k-steps of S = Q K^T
+  static constexpr int DBLK = D / 32;                    // 32-dim blocks of dK^T, dV^T
+  static_assert((2 * DMAS) % WAVES == 0, "tile loads must split evenly over the waves");
 };
 
-// Chunk swizzle of the 32-row Q and dO tiles: the 16-byte chunk index of row r is XORed with
-// constants for row bits 0, 1, 3 and 4 (bit 2 never varies within one read).  A 16-byte read of S
-// or dP has the 16 lanes of a group at rows 8 a + 4 b + c (a = L / 4, c = L % 4, one b) and one
-// chunk per group; a transposing read has each group at rows 8 G + 4 I + c and one 32-byte piece.
-// The constants were chosen against this chip's measured LDS behaviour rather than a plain
-// 64-bank model: the bank of a dword is address bits 2-7 XOR address bits 10-15, and a 16-byte
-// read is served 8 lanes at a time, the lanes that agree in lane bits 2, 4 and 5.  Under that
-// model (which reproduces the conflict counts of 64 measured candidates and of the other kernels'
-// layouts) both read patterns are free of bank conflicts at d = 128 and d = 64; the previous
-// swizzle, conflict-free under the plain model, cost the 16-byte reads two cycles each at d = 128.
-template <int D>
-__device__ __forceinline__ int qswz(int row);
-template <>
-__device__ __forceinline__ int qswz<128>(int row) {
-  return ((row & 1) ? 7 : 0) ^ ((row & 2) ? 10 : 0) ^ ((row & 8) ? 4 : 0) ^ ((row & 16) ? 5 : 0);
-}
-template <>
-__device__ __forceinline__ int qswz<64>(int row) {
-  return ((row & 2) ? 2 : 0) ^ ((row & 8) ? 4 : 0) ^ ((row & 16) ? 1 : 0);
-}
-
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, int64_t rows_total,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H, int group, int Nq, int Nk, int n_kblk,
     float scale, float sl2, int diag) {
   using C = DkvCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char qb[2][C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char ob[2][C::TILE_BYTES];
-  __shared__ __attribute__((aligned(256))) float sb[2][2 * C::BQ];  // [L2 x 32][Dr x 32]
+  // One array per slot and tensor: the compiler then tells a slot being read from the one a load is
+  // filling, and waits for a tile's loads only where that tile is read.  All of them lie below
+  // 64 KiB, in reach of the ds_read immediate offset.
+  __shared__ __attribute__((aligned(1024))) char q0b[C::TILE_BYTES], q1b[C::TILE_BYTES], q2b[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char o0b[C::TILE_BYTES], o1b[C::TILE_BYTES], o2b[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) float s0b[2 * C::BQ], s1b[2 * C::BQ], s2b[2 * C::BQ];  // [L2][Dr]
+  auto qslot = [&](auto I) -> char* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return q0b;
+    else if constexpr (i == 1) return q1b;
+    else return q2b;
+  };
+  auto oslot = [&](auto I) -> char* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return o0b;
+    else if constexpr (i == 1) return o1b;
+    else return o2b;
+  };
+  auto sslot = [&](auto I) -> float* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return s0b;
+    else if constexpr (i == 1) return s1b;
+    else return s2b;
+  };
 
   const int item = xcd_item();
   const int kblk = item % n_kblk;
   const int bkv = item / n_kblk;  // b * H_kv + kv head
   const int H_kv = H / group;
   const int b = bkv / H_kv, hk = bkv % H_kv;
-  const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, L = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k0 = kblk * C::BK;
-  const int key = k0 + wave * 16 + L;  // this lane's key (column of every accumulator)
+  const int kw0 = k0 + wave * 32;  // the wave's first key
+  const int key = kw0 + l32;       // this lane's key (column of every accumulator)
   const int keyc = min(key, Nk - 1);
 
-  // K^T and V^T fragments (B operands of S and dP): key `key`, dims 32 ks + 8 G .. + 7
-  bf16x8_t kf[C::KS], vf[C::KS];
+  // K^T and V^T fragments (B operands of S and dP): key `key`, dims 16 ks + 8 hh .. + 7
+  bf16x8_t kf[C::KSTEPS], vf[C::KSTEPS];
   {
-    const uint16_t* kp = K + ((int64_t)bkv * Nk + keyc) * D + 8 * G;
-    const uint16_t* vp = V + ((int64_t)bkv * Nk + keyc) * D + 8 * G;
+    const uint16_t* kp = K + ((int64_t)bkv * Nk + keyc) * D + 8 * hh;
+    const uint16_t* vp = V + ((int64_t)bkv * Nk + keyc) * D + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      kf[ks] = as_bf16x8(gload16(kp + 32 * ks));
-      vf[ks] = as_bf16x8(gload16(vp + 32 * ks));
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      kf[ks] = as_bf16x8(gload16(kp + 16 * ks));
+      vf[ks] = as_bf16x8(gload16(vp + 16 * ks));
+      // only ever MFMA operands: kept in the accumulation registers, leaving the VGPRs to the
+      // two tiles of S and dP the VALU works on
+      asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
     }
   }
 
-  // LDS offsets.  S and dP: A row r = L of 16-row block bl reads query 8 (r / 4) + 4 bl + r % 4
-  // of the tile, so accumulator register j of block bl in lane group G is query 8 G + 4 bl + j and
-  // the 8 values a lane holds are the B operand (k = queries 8 G .. 8 G + 7) of dV^T and dK^T.
-  int roff[2][C::KS];
+  // LDS offsets.  S and dP: MFMA row m reads query key_of_row(m) of the tile, so register j of
+  // lane-half hh of S and dP is query 16 (j / 8) + 8 hh + j % 8 and 8 consecutive registers,
+  // packed to bf16, are the B operand (k = those queries) of dV^T and dK^T.  Their A operands,
+  // dO^T and Q^T, come from the transposing ds_read_b64_tr_b16: lane l receives dim
+  // 32 mb + l % 32 of queries 16 t2 + 8 hh .. + 7 (t2 the k-step).
+  int roff[C::KSTEPS];
+  {
+    const int qrow = key_of_row(l32);
 #pragma unroll
-  for (int bl = 0; bl < 2; ++bl) {
-    const int row = 8 * (L >> 2) + 4 * bl + (L & 3);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) roff[bl][ks] = row * C::RB + (((4 * ks + G) ^ qswz<D>(row)) << 4);
+    for (int ks = 0; ks < C::KSTEPS; ++ks) roff[ks] = qrow * C::RB + (((2 * ks + hh) ^ swz<D>(qrow)) << 4);
   }
-  // transposing reads for dO^T and Q^T (A of dV^T, dK^T): lane L of group G addresses query
-  // 8 G + 4 I + L / 4, dims 16 db + 4 (L % 4) .. + 3 (byte 32 db + 8 (L % 4) of the row); lane l
-  // receives dim 16 db + L of queries 8 G + 4 I .. + 3
-  auto tr_off = [&](int I, int db) {
-    const int row = 8 * G + 4 * I + (L >> 2);
-    return row * C::RB + (((2 * db + ((L & 3) >> 1)) ^ qswz<D>(row)) << 4) + ((L & 1) ? 8 : 0);
-  };
-
-  f32x4v_t dk[C::DB], dv[C::DB];
+  int toff[C::DBLK][2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const int vh = g >> 1, ve = s >> 2, vq = s & 3;
 #pragma unroll
-  for (int i = 0; i < C::DB; ++i) {
-    dk[i] = f32x4v_t{};
-    dv[i] = f32x4v_t{};
+    for (int mb = 0; mb < C::DBLK; ++mb)
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        const int row = 8 * vh + 4 * I + ve;
+        const int dim = 32 * mb + 16 * (g & 1) + 4 * vq;
+        toff[mb][I] = row * C::RB + (((dim >> 3) ^ swz<D>(row)) << 4) + ((dim >> 2) & 1) * 8;
+      }
   }
 
-  // query tiles this workgroup's keys can be seen from: query i sees key j iff j <= i + diag
+  f32x16_t dk[C::DBLK], dv[C::DBLK];
+#pragma unroll
+  for (int mb = 0; mb < C::DBLK; ++mb) {
+    dk[mb] = f32x16_t{};
+    dv[mb] = f32x16_t{};
+  }
+
+  // query tiles this workgroup's keys can be seen from: query i sees key j iff j <= i + diag;
+  // they are visited from the last one down, so that the workgroups of one head (all on one XCD)
+  // read the same tile at about the same time whatever their first tile
   const int q_first = CAUSAL ? max(0, k0 - diag) / C::BQ : 0;
   const int n_qt = (Nq + C::BQ - 1) / C::BQ;
-  const __amdgpu_buffer_rsrc_t wsr = raw_rsrc(ws, (int)(2 * rows_total * 4));
+  const int n_steps = n_qt - q_first;
+  // the statistics load takes L2 in lanes 0-31 and Dr in lanes 32-63
+  const int stat_off = (int)((hh * rows_total + l32) * 4);
+
+  auto bar = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // wait until at most n of this wave's vector memory loads are outstanding
+  auto wait_loads_but = [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+  };
+
+  f32x16_t S[2], DP[2];  // S and dP of two tiles: the one the VALU consumes, the one the MFMAs fill
+  u32x4_t pB[2], dsB[2];
 
   for (int gh = 0; gh < group; ++gh) {
+    if (n_steps <= 0) break;
     const int bh = b * H + hk * group + gh;  // query head
     const uint16_t* Qh = Q + (int64_t)bh * Nq * D;
     const uint16_t* Oh = dO + (int64_t)bh * Nq * D;
-    const __amdgpu_buffer_rsrc_t Qr = raw_rsrc(Qh, Nq * C::RB), Or = raw_rsrc(Oh, Nq * C::RB);
-    auto issue = [&](int t, int buf) {
+    // Tile t's loads, each tensor through a buffer resource based at the tile's first row with its
+    // range ending at the head's last row (the statistics': at the workspace's end), so a lane's
+    // offset is the same for every tile and rows past the last query read as zero.  Instruction i
+    // of this wave moves 1 KiB of Q (x < DMAS) or dO, lane L landing in row L / CPR, slot L % CPR
+    // of the instruction's rows and fetching the chunk the swizzle puts there.  The last wave also
+    // moves the statistics.
+    auto issue = [&](int t, auto SLOT) {
+      const int r0 = t * C::BQ;
+      const __amdgpu_buffer_rsrc_t Qr = raw_rsrc(Qh + (int64_t)r0 * D, (Nq - r0) * C::RB);
+      const __amdgpu_buffer_rsrc_t Or = raw_rsrc(Oh + (int64_t)r0 * D, (Nq - r0) * C::RB);
 #pragma unroll
       for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
         const int x = wave + C::WAVES * i;
-        if (x < 2 * C::DMAS) {
-          const int c = x < C::DMAS ? x : x - C::DMAS;
-          const int row = c * C::ROWS_PER_DMA + lane / C::CPR;
-          const uint32_t off =
-              (uint32_t)min(t * C::BQ + row, Nq - 1) * C::RB + (((lane % C::CPR) ^ qswz<D>(row)) << 4);
-          if (x < C::DMAS)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(Qr, (lptr_t)(qb[buf] + c * 1024), 16, off, 0, 0, 0);
-          else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(Or, (lptr_t)(ob[buf] + c * 1024), 16, off, 0, 0, 0);
-        }
+        const int c = x % C::DMAS;
+        const int row = c * C::ROWS_PER_DMA + lane / C::CPR;
+        const int off = row * C::RB + (((lane % C::CPR) ^ swz<D>(row)) << 4);
+        if (x < C::DMAS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(Qr, (lptr_t)(qslot(SLOT) + c * 1024), 16, off, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(Or, (lptr_t)(oslot(SLOT) + c * 1024), 16, off, 0, 0, 0);
       }
-      if (wave == C::WAVES - 1) {  // L2 (lanes 0-31) and Dr (lanes 32-63) of the tile's queries
-        const int qq = min(t * C::BQ + (lane & 31), Nq - 1);
-        const uint32_t off = (uint32_t)(((lane >> 5) * rows_total + (int64_t)bh * Nq + qq) * 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (lptr_t)(&sb[buf][0]), 4, off, 0, 0, 0);
+      if (wave == C::WAVES - 1) {
+        const int64_t e0 = (int64_t)bh * Nq + r0;
+        const __amdgpu_buffer_rsrc_t Sr = raw_rsrc(ws + e0, (int)((2 * rows_total - e0) * 4));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(Sr, (lptr_t)sslot(SLOT), 4, stat_off, 0, 0, 0);
       }
     };
+    auto tile_of = [&](int k) { return n_qt - 1 - k; };
 
-    // One 32-query tile with its LDS slot fixed at compile time (the loop below alternates the
-    // two), so every LDS address is a per-lane base plus an immediate.  Only tiles that reach past
-    // the wave's diagonal or the end of the queries are masked element by element.
-    // Query tiles are visited from the last one down, so that the workgroups of one head (all on
-    // one XCD) read the same tile at about the same time whatever their first tile.
-    auto tile = [&](int t, auto slot) {
-      constexpr int cur = decltype(slot)::value;
-      if (t - 1 >= q_first) issue(t - 1, cur ^ 1);
-      const FA_LDS char* qt = (const FA_LDS char*)qb[cur];
-      const FA_LDS char* ot = (const FA_LDS char*)ob[cur];
-      const FA_LDS float* st = (const FA_LDS float*)sb[cur];
-      // S = Q K^T and dP = dO V^T as an explicit pipeline: MFMA i (k-step i / 4, block (i / 2) % 2,
-      // S for even i, dP for odd) reads its A operand FA_BWD_LOOKAHEAD MFMAs ahead, since a
-      // 16-cycle MFMA cannot cover an LDS read on its own; the four accumulators alternate.
-      constexpr int LA = FA_BWD_LOOKAHEAD;
-      f32x4v_t s[2], dp[2];
-#pragma unroll
-      for (int bl = 0; bl < 2; ++bl) {
-        s[bl] = f32x4v_t{};
-        dp[bl] = f32x4v_t{};
-      }
-      {
-        constexpr int NA = 4 * C::KS;
-        u32x4_t fa[LA + 1];
-        auto read_a = [&](auto I) {
-          constexpr int i = decltype(I)::value;
-          fa[i % (LA + 1)] = lds_load16(((i & 1) ? ot : qt) + roff[(i >> 1) & 1][i >> 2]);
-        };
-        static_for<LA>([&](auto I) { read_a(I); });
-        static_for<NA>([&](auto I) {
-          constexpr int i = decltype(I)::value, bl = (i >> 1) & 1, ks = i >> 2;
-          if constexpr (i & 1)
-            dp[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fa[i % (LA + 1)]), vf[ks], dp[bl], 0, 0, 0);
-          else
-            s[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fa[i % (LA + 1)]), kf[ks], s[bl], 0, 0, 0);
-          if constexpr (i + LA < NA) read_a(std::integral_constant<int, i + LA>{});
-          __builtin_amdgcn_sched_barrier(0);
+    // One step: the S / dP MFMAs of tile k + 1 (slot SN, into set 1 - RC) with P and dS of tile
+    // k (set RC, statistics of slot SC) on the VALU between them, then dV^T += dO^T P and
+    // dK^T += Q^T dS from tile k's slot.  MFMA i < 16 is k-step i / 2 of S (even) or dP (odd);
+    // MFMA 16 + i is k-step t2 = i / (2 DBLK) of dim block (i / 2) % DBLK, dV (even) or dK.
+    // Every operand read runs LA MFMAs ahead.  The last step computes S and dP of a stale slot
+    // and drops them, so that every step has the same schedule.
+    auto body = [&](auto SC, auto SN, auto RC) {
+      constexpr int rc = decltype(RC)::value, rn = 1 - rc;
+      constexpr int LA = FA_BWD_LOOKAHEAD, NA = 2 * C::KSTEPS, NC = 4 * C::DBLK, N = NA + NC;
+      const FA_LDS char* qn = (const FA_LDS char*)qslot(SN);
+      const FA_LDS char* on = (const FA_LDS char*)oslot(SN);
+      const FA_LDS char* qc = (const FA_LDS char*)qslot(SC);
+      const FA_LDS char* oc = (const FA_LDS char*)oslot(SC);
+      const FA_LDS float* st = (const FA_LDS float*)sslot(SC);
+      u32x4_t fr[LA + 1];
+      auto read = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < NA) {
+          fr[i % (LA + 1)] = lds_load16(((i & 1) ? on : qn) + roff[i >> 1]);
+        } else {
+          constexpr int c = i - NA, t2 = c / (2 * C::DBLK), mb = (c >> 1) % C::DBLK;
+          const FA_LDS char* base = ((c & 1) ? qc : oc) + t2 * 16 * C::RB;
+          const i16x4_t lo = lds_load8_tr16(base + toff[mb][0]);
+          const i16x4_t hi = lds_load8_tr16(base + toff[mb][1]);
+          fr[i % (LA + 1)] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      };
+      // P and dS of tile k in eight units of two elements (unit w: j = 2 w, 2 w + 1, queries
+      // 16 t2 + 8 hh + 2 u + e), each in four stages one MFMA slot apart, so that no slot waits for
+      // a result of its own: A the exponent and dP - Dr, B the exponentials, C dS and the packed
+      // P, D the packed dS.  Unit w starts at slot G w; its L2 and Dr are read three slots earlier.
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      constexpr int G = NA / 8;
+      f32x2_t l2u[8], dru[8], ta[8], da[8], pa[8], dsa[8];
+      auto stats = [&](auto W) {
+        constexpr int w = decltype(W)::value, t2 = w >> 2, u = w & 3;
+        l2u[w] = *(const FA_LDS f32x2_t*)(st + 16 * t2 + 8 * hh + 2 * u);
+        dru[w] = *(const FA_LDS f32x2_t*)(st + C::BQ + 16 * t2 + 8 * hh + 2 * u);
+      };
+      auto stage = [&](auto W, auto X) {
+        constexpr int w = decltype(W)::value, x = decltype(X)::value, t2 = w >> 2, u = w & 3, j = 8 * t2 + 2 * u;
+        if constexpr (x == 0) {
+          ta[w][0] = __builtin_fmaf(S[rc][j], sl2, -l2u[w][0]);
+          ta[w][1] = __builtin_fmaf(S[rc][j + 1], sl2, -l2u[w][1]);
+          da[w][0] = DP[rc][j] - dru[w][0];
+          da[w][1] = DP[rc][j + 1] - dru[w][1];
+        } else if constexpr (x == 1) {
+          pa[w][0] = fast_exp2(ta[w][0]);
+          pa[w][1] = fast_exp2(ta[w][1]);
+        } else if constexpr (x == 2) {
+          dsa[w][0] = pa[w][0] * da[w][0];
+          dsa[w][1] = pa[w][1] * da[w][1];
+          pB[t2][u] = pack_bf16x2(pa[w][0], pa[w][1]);
+        } else {
+          dsB[t2][u] = pack_bf16x2(dsa[w][0], dsa[w][1]);
+        }
+      };
+      // the work of slot i (i = -1: before the first MFMA)
+      auto valu_slot = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        static_for<8>([&](auto W) {
+          constexpr int w = decltype(W)::value, s0 = G * w;
+          if constexpr ((s0 - 3 < 0 ? -1 : s0 - 3) == i) stats(W);
+          static_for<4>([&](auto X) {
+            if constexpr (s0 + decltype(X)::value == i) stage(W, X);
+          });
         });
-      }
-      // the first transposing reads of dV^T / dK^T go out now, under the P and dS arithmetic
-      constexpr int NC = 2 * C::DB;
-      u32x4_t fc[LA + 1];
-      auto read_c = [&](auto I) {  // MFMA i: dV^T block i / 2 (even i, from dO) or dK^T (odd, from Q)
-        constexpr int i = decltype(I)::value, db = i >> 1;
-        const FA_LDS char* base = (i & 1) ? qt : ot;
-        const i16x4_t lo = lds_load8_tr16(base + tr_off(0, db));
-        const i16x4_t hi = lds_load8_tr16(base + tr_off(1, db));
-        fc[i % (LA + 1)] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      static_for<LA>([&](auto I) { read_c(I); });
-      __builtin_amdgcn_sched_barrier(0);
-      // P and dS for queries q0 + 8 G + 4 bl + j against this lane's key
-      const int q0 = t * C::BQ;
-      const f32x4v_t l2a = *(const FA_LDS f32x4v_t*)(st + 8 * G);
-      const f32x4v_t l2b = *(const FA_LDS f32x4v_t*)(st + 8 * G + 4);
-      const f32x4v_t dra = *(const FA_LDS f32x4v_t*)(st + C::BQ + 8 * G);
-      const f32x4v_t drb = *(const FA_LDS f32x4v_t*)(st + C::BQ + 8 * G + 4);
-      const bool masked = (q0 + C::BQ > Nq) || (CAUSAL && k0 + wave * 16 + 15 > q0 + diag);
-      u32x4_t pB, dsB;
-      auto p_ds = [&](auto mask_tag) {
-#pragma unroll
-        for (int bl = 0; bl < 2; ++bl)
-#pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2) {
-            float pv[2], dsv[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int j = 2 * j2 + e;
-              const float l2 = bl ? l2b[j] : l2a[j];
-              const float dr = bl ? drb[j] : dra[j];
-              float p = fast_exp2(__builtin_fmaf(s[bl][j], sl2, -l2));
-              if constexpr (decltype(mask_tag)::value) {
-                const int qq = q0 + 8 * G + 4 * bl + j;
-                asm volatile("" : "+v"(p));  // a select, not a branch around the exponential per element
-                p = (qq >= Nq || (CAUSAL && key > qq + diag)) ? 0.f : p;
-              }
-              pv[e] = p;
-              dsv[e] = p * (dp[bl][j] - dr);
-            }
-            pB[2 * bl + j2] = pack_bf16x2(pv[0], pv[1]);
-            dsB[2 * bl + j2] = pack_bf16x2(dsv[0], dsv[1]);
-          }
-      };
-      if (masked)
-        p_ds(std::true_type{});
-      else
-        p_ds(std::false_type{});
-      // dV^T += dO^T P,  dK^T += Q^T dS  (k = the tile's 32 queries), reads LA MFMAs ahead
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<NC>([&](auto I) {
-        constexpr int i = decltype(I)::value, db = i >> 1;
-        if constexpr (i & 1)
-          dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fc[i % (LA + 1)]), as_bf16x8(dsB), dk[db], 0, 0, 0);
-        else
-          dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fc[i % (LA + 1)]), as_bf16x8(pB), dv[db], 0, 0, 0);
-        if constexpr (i + LA < NC) read_c(std::integral_constant<int, i + LA>{});
+      S[rn] = f32x16_t{};
+      DP[rn] = f32x16_t{};
+      valu_slot(std::integral_constant<int, -1>{});
+      static_for<LA>([&](auto I) { read(I); });
+      static_for<N>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < NA) {
+          if constexpr (i & 1)
+            DP[rn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[i % (LA + 1)]), vf[i >> 1], DP[rn], 0, 0, 0);
+          else
+            S[rn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[i % (LA + 1)]), kf[i >> 1], S[rn], 0, 0, 0);
+        } else {
+          constexpr int c = i - NA, t2 = c / (2 * C::DBLK), mb = (c >> 1) % C::DBLK;
+          if constexpr (c & 1)
+            dk[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[i % (LA + 1)]), as_bf16x8(dsB[t2]), dk[mb], 0, 0, 0);
+          else
+            dv[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[i % (LA + 1)]), as_bf16x8(pB[t2]), dv[mb], 0, 0, 0);
+        }
+        if constexpr (i + LA < N) read(std::integral_constant<int, i + LA>{});
+        valu_slot(I);
         __builtin_amdgcn_sched_barrier(0);
       });
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
+      asm volatile("" : "+v"(S[rn]), "+v"(DP[rn]));
     };
 
-    if (q_first < n_qt) issue(n_qt - 1, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    int t = n_qt - 1;
-    for (; t - 1 >= q_first; t -= 2) {
-      tile(t, std::integral_constant<int, 0>{});
-      tile(t - 1, std::integral_constant<int, 1>{});
+    // Step k (tile k is in slot k % 3 and its S / dP in set k % 2): wait for tile k + 1, meet the
+    // other waves (all past step k - 1, so the slot of tile k - 1 is free), start tile k + 2 into
+    // it, then the body.
+    auto step = [&](int k, auto P) {
+      constexpr int p = decltype(P)::value;
+      wait_loads_but(std::integral_constant<int, 0>{});
+      bar();
+      if (k + 2 < n_steps) issue(tile_of(k + 2), std::integral_constant<int, (p + 2) % C::SLOTS>{});
+      // a tile that reaches past the wave's diagonal or the end of the queries: its masked
+      // scores become -inf, so that P and dS are 0 there
+      const int q0 = tile_of(k) * C::BQ;
+      if ((q0 + C::BQ > Nq) || (CAUSAL && kw0 + 31 > q0 + diag)) {
+        constexpr int rc = p % 2;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int qq = q0 + 16 * (j >> 3) + 8 * hh + (j & 7);
+          if (qq >= Nq || (CAUSAL && key > qq + diag)) S[rc][j] = -INFINITY;
+        }
+      }
+      body(std::integral_constant<int, p % C::SLOTS>{}, std::integral_constant<int, (p + 1) % C::SLOTS>{},
+           std::integral_constant<int, p % 2>{});
+    };
+
+    // prologue: tiles 0 and 1 into slots 0 and 1 (after every wave has left the previous head's
+    // slots), and S / dP of tile 0 into set 0
+    bar();
+    issue(tile_of(0), std::integral_constant<int, 0>{});
+    if (n_steps > 1) issue(tile_of(1), std::integral_constant<int, 1>{});
+    wait_loads_but(std::integral_constant<int, 0>{});
+    bar();
+    {
+      constexpr int LA = FA_BWD_LOOKAHEAD, NA = 2 * C::KSTEPS;
+      const FA_LDS char* q0t = (const FA_LDS char*)q0b;
+      const FA_LDS char* o0t = (const FA_LDS char*)o0b;
+      u32x4_t fr[LA + 1];
+      auto read = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        fr[i % (LA + 1)] = lds_load16(((i & 1) ? o0t : q0t) + roff[i >> 1]);
+      };
+      S[0] = f32x16_t{};
+      DP[0] = f32x16_t{};
+      static_for<LA>([&](auto I) { read(I); });
+      static_for<NA>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i & 1)
+          DP[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[i % (LA + 1)]), vf[i >> 1], DP[0], 0, 0, 0);
+        else
+          S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[i % (LA + 1)]), kf[i >> 1], S[0], 0, 0, 0);
+        if constexpr (i + LA < NA) read(std::integral_constant<int, i + LA>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      asm volatile("" : "+v"(S[0]), "+v"(DP[0]));
     }
-    if (t >= q_first) tile(t, std::integral_constant<int, 0>{});
+    for (int k = 0;;) {
+      step(k, std::integral_constant<int, 0>{});
+      if (++k >= n_steps) break;
+      step(k, std::integral_constant<int, 1>{});
+      if (++k >= n_steps) break;
+      step(k, std::integral_constant<int, 2>{});
+      if (++k >= n_steps) break;
+      step(k, std::integral_constant<int, 3>{});
+      if (++k >= n_steps) break;
+      step(k, std::integral_constant<int, 4>{});
+      if (++k >= n_steps) break;
+      step(k, std::integral_constant<int, 5>{});
+      if (++k >= n_steps) break;
+    }
   }
 
-  // dK = scale dK^T^T, dV = dV^T^T: register j of block db is dim 16 db + 4 G + j of key `key`
+  // dK = scale (dK^T)^T, dV = (dV^T)^T: register 4 jg + i of block mb is dim 32 mb + 8 jg + 4 hh + i
   if (key < Nk) {
-    uint16_t* kp = dK + ((int64_t)bkv * Nk + key) * D + 4 * G;
-    uint16_t* vp = dV + ((int64_t)bkv * Nk + key) * D + 4 * G;
+    uint16_t* kp = dK + ((int64_t)bkv * Nk + key) * D + 4 * hh;
+    uint16_t* vp = dV + ((int64_t)bkv * Nk + key) * D + 4 * hh;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      u32x2_t wk, wv;
-      wk[0] = pack_bf16x2(dk[db][0] * scale, dk[db][1] * scale);
-      wk[1] = pack_bf16x2(dk[db][2] * scale, dk[db][3] * scale);
-      wv[0] = pack_bf16x2(dv[db][0], dv[db][1]);
-      wv[1] = pack_bf16x2(dv[db][2], dv[db][3]);
-      *(u32x2_t*)(kp + 16 * db) = wk;
-      *(u32x2_t*)(vp + 16 * db) = wv;
-    }
+    for (int mb = 0; mb < C::DBLK; ++mb)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        u32x2_t wk, wv;
+        wk[0] = pack_bf16x2(dk[mb][4 * jg + 0] * scale, dk[mb][4 * jg + 1] * scale);
+        wk[1] = pack_bf16x2(dk[mb][4 * jg + 2] * scale, dk[mb][4 * jg + 3] * scale);
+        wv[0] = pack_bf16x2(dv[mb][4 * jg + 0], dv[mb][4 * jg + 1]);
+        wv[1] = pack_bf16x2(dv[mb][4 * jg + 2], dv[mb][4 * jg + 3]);
+        *(u32x2_t*)(kp + 32 * mb + 8 * jg) = wk;
+        *(u32x2_t*)(vp + 32 * mb + 8 * jg) = wv;
+      }
   }
 }
 
