@@ -2,7 +2,8 @@
 //
 // Decode is a matrix-vector product bound by reading the KV cache from HBM (Day-21 page
 // "GPU 学习日报 Day 21：FlashAttention：GPU Memory Hierarchy 下的 IO 优化", §9 and FAQ Q5), so
-// there is no MFMA here: the work is spread over many workgroups by splitting the keys into
+// one query head per K/V head runs on the VALU; only grouped heads (several query rows per K/V
+// row) use the matrix core.  The work is spread over many workgroups by splitting the keys into
 // contiguous chunks that are processed in parallel and merged afterwards (Q31 answer
 // "FlashAttention 为什么快", follow-up 3).  The merge rescales every partial result by
 // exp(m_s - max m) before summing (same answer, follow-up 2).
@@ -13,8 +14,8 @@
 // rescaled accumulator, Day-21 page §5.2-5.3), U key rows of K and of V in flight per lane.
 // With grouped K/V heads (several query heads per K/V head, which the Day-21 page's FAQ Q5
 // names among the decode-side techniques) a workgroup serves up to four query heads from one
-// read of the K/V rows.  The four waves' states are merged through LDS and written to the
-// workspace as (O_part, m, l) per query head.
+// read of the K/V rows (for bf16: decode_split_mfma_kernel).  The four waves' states are merged
+// through LDS and written to the workspace as (O_part, m, l) per query head.
 // decode_combine_kernel: one workgroup per (batch*head), one thread per dim.
 #include <atomic>
 
@@ -29,6 +30,8 @@ namespace {
 __device__ __forceinline__ u32x4_t stream_load16(const void* p) {
   return __builtin_nontemporal_load((const u32x4_t*)p);
 }
+// The same hint as the cache-policy operand of a buffer load (the NT bit)
+constexpr int kNonTemporal = 2;
 
 // x from lane CTRL-permuted within its row.  Every pattern used here reads a valid lane, so
 // bound_ctrl is set: that lets the compiler fold the move into the add that consumes it
@@ -251,6 +254,198 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
   }
 }
 
+// Grouped decode on the matrix core (bf16 K/V, GE = 2 or 4 query heads per K/V head).  With
+// several query heads per K/V row, the kernel above spends most of its time on per-head dot
+// products and accumulations on the VALU; here both products run on v_mfma_f32_16x16x32_bf16,
+// with the GE query rows padded to 16:
+//  * S^T = K Q^T, one 16-key tile by 16 query columns per MFMA.  Lane l takes key row l % 16 of
+//    the tile and dims 32 ks + 8 (l / 16) .. + 7 of it as its A operand straight from HBM (each
+//    row group of four lanes reads 64 contiguous bytes per k-step), and the same dims of query
+//    l % 16 as B.  The accumulator gives lane l query l % 16 against keys 4 (l / 16) .. + 3.
+//  * One exact row max per 32-key trip (in the lane, then over the four lane groups), and P =
+//    exp2(S scale log2 e - m) packed to bf16 straight from the accumulators: the keys
+//    16 (e / 4) + 4 (l / 16) + e % 4 of the trip (e = 0..7) that lane l holds are its B operand of
+//  * O^T += V^T P^T, 16 dims by 16 query columns per MFMA.  V goes by LDS DMA into a buffer of
+//    the wave's own, and its A operand (dim 16 mb + l % 16 of those same eight keys) comes from
+//    two transposing ds_read_b64_tr_b16 reads.  O^T's lane l holds query l % 16, so the rescale by
+//    exp2(m_old - m_new) is a per-lane scalar.
+// Rows of the V buffers are XOR-swizzled in 16-byte chunks by the row's low bits.  K registers and
+// V buffers are double-buffered, so each wave has its next trip's rows in flight while it computes
+// the current one (its K rows from the trip's start, its V rows from the trip's PV products on).  The four waves merge their states through LDS as in the kernel above and write
+// the same partials.
+#ifndef FA_DEC_TRIP
+#define FA_DEC_TRIP 32  // keys per wave per trip of the matrix-core decode split
+#endif
+
+template <int D, int GE>
+__global__ __launch_bounds__(256) void decode_split_mfma_kernel(const uint16_t* __restrict__ Q,
+                                                                const uint16_t* __restrict__ K,
+                                                                const uint16_t* __restrict__ V,
+                                                                float* __restrict__ Opart, float* __restrict__ ML,
+                                                                int Nk, int S, int chunk, float sl2, int H, int group) {
+  constexpr int WAVES = 4, TK = FA_DEC_TRIP;  // keys per wave per trip
+  constexpr int NT = TK / 16, NKK = TK / 32;  // 16-key tiles of S^T, 32-key k-steps of O^T per trip
+  constexpr int RB = D * 2, CPR = D / 8;      // bytes and 16-byte chunks per key row
+  constexpr int KS = D / 32;                  // k-steps of S^T
+  constexpr int DB = D / 16;                  // 16-dim blocks of O^T
+  constexpr int VDMA = TK * RB / 1024;        // 1 KiB LDS loads per V tile
+  static_assert(GE == 2 || GE == 4, "two or four query heads per workgroup");
+  static_assert(TK % 32 == 0, "whole k-steps of O^T");
+  __shared__ __attribute__((aligned(1024))) char vbuf[WAVES][TK * RB];
+  __shared__ float s_m[WAVES][GE], s_l[WAVES][GE];
+  __shared__ float s_acc[WAVES][GE][D];
+
+  const int s = blockIdx.x % S;
+  const int bh0 = (blockIdx.x / S) * GE;  // first query head (b * H + h) of this workgroup's group
+  const int start = s * chunk;
+  const int end = min(Nk, start + chunk);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the V loads' resource and LDS base
+  const int c16 = lane & 15, G = lane >> 4;
+  const int kvh = (bh0 / H) * (H / group) + (bh0 % H) / group;  // K/V head shared by the GE query heads
+  const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
+  const uint16_t* Vh = V + (int64_t)kvh * Nk * D;
+
+  // Q^T (B operand of S^T): query c16 (zero columns past GE), dims 32 ks + 8 G .. + 7
+  u32x4_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
+  if (c16 < GE) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = gload16(Q + (int64_t)(bh0 + c16) * D + 32 * ks + 8 * G);
+  }
+  // transposing V reads: lane (G, c16) of read (mb, I) addresses row 16 I + 4 G + c16 / 4 of a
+  // 32-key k-step, dims 16 mb + 4 (c16 % 4) .. + 3, and receives dim 16 mb + c16 of its four rows
+  int voff[DB][2];
+#pragma unroll
+  for (int mb = 0; mb < DB; ++mb)
+#pragma unroll
+    for (int I = 0; I < 2; ++I) {
+      const int row = 16 * I + 4 * G + (c16 >> 2);
+      const int byte = (16 * mb + 4 * (c16 & 3)) * 2;
+      voff[mb][I] = row * RB + (((byte >> 4) ^ (row % CPR)) << 4) + (byte & 15);
+    }
+
+  f32x4_t oT[DB];  // O^T: query c16, dims 16 mb + 4 G + j
+#pragma unroll
+  for (int mb = 0; mb < DB; ++mb) oT[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // running max (log2 units) of query c16, this lane's share of its sum
+  const FA_LDS char* vb = (const FA_LDS char*)vbuf[wave];
+
+  for (int base = start + wave * TK; base < end; base += WAVES * TK) {
+    // K rows into the A operands of S^T (tile t, k-step ks: key row base + 16 t + c16, dims
+    // 32 ks + 8 G), then the V rows into the wave's buffer by LDS DMA (instruction i moves 1 KiB,
+    // lane L landing in row (1024 i + 16 L) / RB, slot L % CPR, which holds the row's chunk
+    // (L % CPR) ^ (row % CPR); rows past the last key read as zero)
+    u32x4_t kr[NT][KS];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint16_t* kp = Kh + (int64_t)min(base + 16 * t + c16, Nk - 1) * D + 8 * G;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kr[t][ks] = stream_load16(kp + 32 * ks);
+    }
+    {
+      const __amdgpu_buffer_rsrc_t vr = raw_rsrc(Vh + (int64_t)base * D, (Nk - base) * RB);
+#pragma unroll
+      for (int i = 0; i < VDMA; ++i) {
+        const int row = (i * 1024 + lane * 16) / RB;
+        const int off = row * RB + (((lane % CPR) ^ (row % CPR)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lptr_t)(vbuf[wave] + i * 1024), 16, off, 0, 0, kNonTemporal);
+      }
+    }
+    f32x4_t st[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[t][ks]), as_bf16x8(qf[ks]), st[t], 0, 0, 0);
+    }
+    if (base + TK > end) {  // keys past the split's end
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (base + 16 * t + 4 * G + j >= end) st[t][j] = -INFINITY;
+    }
+    // the trip's max of query c16: in the lane, then over the four lane groups
+    float mx = st[0][0];
+#pragma unroll
+    for (int x = 1; x + 1 < 4 * NT; x += 2) mx = max3f(mx, st[x / 4][x % 4], st[(x + 1) / 4][(x + 1) % 4]);
+    mx = fmaxf(mx, st[NT - 1][3]);
+    mx = xor_max<32>(xor_max<16>(mx));
+    const float mnew = fmaxf(m, mx * sl2);
+    const float nm = -mnew;  // the trip holds at least one visible key, so mnew is finite
+    const float alpha = fast_exp2(m + nm);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < DB; ++mb) oT[mb] *= alpha;
+    float p[NT][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[t][j] = fast_exp2(__builtin_fmaf(st[t][j], sl2, nm));
+        ps += p[t][j];
+      }
+    l += ps;
+    // B operand of k-step kk (k = keys 32 kk + 16 (e / 4) + 4 G + e % 4 of the trip, e = 0..7)
+    u32x4_t pb[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      pb[kk][0] = pack_bf16x2(p[2 * kk][0], p[2 * kk][1]);
+      pb[kk][1] = pack_bf16x2(p[2 * kk][2], p[2 * kk][3]);
+      pb[kk][2] = pack_bf16x2(p[2 * kk + 1][0], p[2 * kk + 1][1]);
+      pb[kk][3] = pack_bf16x2(p[2 * kk + 1][2], p[2 * kk + 1][3]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the V rows have landed in this wave's buffer
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < DB; ++mb) {
+        const i16x4_t lo = lds_load8_tr16(vb + kk * 32 * RB + voff[mb][0]);
+        const i16x4_t hi = lds_load8_tr16(vb + kk * 32 * RB + voff[mb][1]);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oT[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[kk]), oT[mb], 0, 0, 0);
+      }
+  }
+  l = xor_sum<32>(xor_sum<16>(l));
+  if (lane < GE) {
+    s_m[wave][lane] = m;
+    s_l[wave][lane] = l;
+  }
+  if (c16 < GE) {
+#pragma unroll
+    for (int mb = 0; mb < DB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_acc[wave][c16][16 * mb + 4 * G + j] = oT[mb][j];
+  }
+  __syncthreads();
+  for (int x = tid; x < GE * D; x += 256) {
+    const int g = x / D, dim = x % D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, s_m[w][g]);
+    float o = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float f = fast_exp2(s_m[w][g] - M);
+        o = __builtin_fmaf(f, s_acc[w][g][dim], o);
+        L = __builtin_fmaf(f, s_l[w][g], L);
+      }
+    }
+    const int64_t rec = (int64_t)(bh0 + g) * S + s;
+    Opart[rec * D + dim] = o;
+    if (dim == 0) {
+      ML[rec * 2] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+      ML[rec * 2 + 1] = L;
+    }
+  }
+}
+
 // Decode split over an FP8 KV cache: K and V rows are OCP E4M3 codes (one byte per element)
 // with one float scale per (batch, K/V head), the value of a code being its E4M3 value times the
 // scale (KV-cache quantisation, which the Day-21 page's FAQ Q5 names among the decode-side
@@ -433,9 +628,22 @@ void launch_split(const DecodeSplitArgs& a, int chunk, float sl2, hipStream_t st
                      a.H / a.H_kv);
 }
 
+template <int D, int GE>
+void launch_split_mfma(const DecodeSplitArgs& a, int chunk, float sl2, hipStream_t stream) {
+  const int64_t nblk = (int64_t)a.B * (a.H / GE) * a.num_splits;
+  hipLaunchKernelGGL((decode_split_mfma_kernel<D, GE>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o_part, a.ml, a.Nk,
+                     a.num_splits, chunk, sl2, a.H, a.H / a.H_kv);
+}
+
 template <typename T, int D>
 void launch_split_d(const DecodeSplitArgs& a, int chunk, float sl2, hipStream_t stream) {
   const int group = a.H / a.H_kv;  // query heads per K/V head; a workgroup takes 4, 2 or 1 of them
+  // bf16 with grouped heads: both products on the matrix core
+  if constexpr (sizeof(T) == 2) {
+    if (group % 4 == 0) return launch_split_mfma<D, 4>(a, chunk, sl2, stream);
+    if (group % 2 == 0) return launch_split_mfma<D, 2>(a, chunk, sl2, stream);
+  }
   if (group % 4 == 0)
     launch_split<T, D, 4>(a, chunk, sl2, stream);
   else if (group % 2 == 0)

@@ -3,12 +3,15 @@ float64 reference: grouped K/V heads and both causal alignments (top-left for an
 bottom-right for a query chunk appended to a KV cache).
 
 Small shapes are compared element by element over the whole output (ragged tiles, Nq < Nk and
-Nq > Nk, one query, several group sizes).  Grouped heads must give bit-for-bit what the same
-kernel gives on K/V with each head repeated, and the extended entry points with H_kv = H must
-give bit-for-bit what fa_fwd / fa_decode_split give.  The full-size chunked-prefill and grouped
+Nq > Nk, one query, several group sizes).  In the forward, grouped heads must give bit-for-bit
+what the same kernel gives on K/V with each head repeated, and the extended entry points with
+H_kv = H must give bit-for-bit what fa_fwd / fa_decode_split give.  The grouped decode split runs
+both products on the matrix core (the ungrouped one on the VALU), so grouped against repeated
+heads is held to the reference's tolerance instead.  The full-size chunked-prefill and grouped
 decode workloads, and shapes with more query blocks than compute units, are compared on every
 head in tests/test_gpu_workloads_all_heads.py."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -115,6 +118,9 @@ DEC_SMALL = [
     _dw("g4_nk5000_s16", 2, 8, 2, 5000, 128, "bf16", 16),
     _dw("g8_nk100_s64_empty", 1, 8, 1, 100, 128, "bf16", 64),
     _dw("g2_nk777_s5_d64", 1, 6, 3, 777, 64, "bf16", 5),
+    _dw("g4_nk50_s3_d64", 1, 4, 1, 50, 64, "bf16", 3),
+    _dw("g2_nk1_s1", 1, 2, 1, 1, 128, "bf16", 1),
+    _dw("g4_nk2049_s4_kv3", 2, 12, 3, 2049, 128, "bf16", 4),
     _dw("f32_g4_nk333_s7", 1, 4, 1, 333, 64, "f32", 7),
 ]
 
@@ -135,12 +141,21 @@ def test_decode_ex_small(w):
     assert_parity(w.dtype, metrics(from_device(o), from_device(lse), o_ref, l_ref), w.name)
 
 
-def test_decode_grouped_equals_repeated_bitwise():
-    w = _dw("dec_gqa_vs_repeat", 2, 8, 2, 3000, 128, "bf16", 16)
-    _, dev = device_inputs(w)
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_grouped_matches_repeated_heads(d):
+    """The grouped split (both products on the matrix core) and the ungrouped split on the same
+    inputs with the K/V heads repeated: each within the decode tolerance of the float64 reference,
+    and the two within twice that of each other."""
+    w = _dw(f"dec_gqa_vs_repeat_d{d}", 2, 8, 2, 3000, d, "bf16", 16)
+    host, dev = device_inputs(w)
     o, lse = _decode_ex(w, dev)
     rep = {x: dev[x].repeat_interleave(w.H // w.kv_heads, dim=1).contiguous() for x in "kv"}
     print("  [fa_decode_split] same inputs, K/V heads repeated", flush=True)
     o2, l2 = fa.decode(dev["q"], rep["k"], rep["v"], w.num_splits, w.scale)
     torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+    o_ref, l_ref = _ref(w, host)
+    assert_parity("bf16", metrics(from_device(o), from_device(lse), o_ref, l_ref), w.name + " grouped")
+    assert_parity("bf16", metrics(from_device(o2), from_device(l2), o_ref, l_ref), w.name + " repeated")
+    og, orp = from_device(o).astype(np.float64), from_device(o2).astype(np.float64)
+    assert np.abs(og - orp).max() <= 4e-2
+    assert np.abs(from_device(lse) - from_device(l2)).max() <= 2e-3
