@@ -45,43 +45,49 @@ def lib() -> ctypes.CDLL:
     """Load libfa.so (once).  Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_attention_126_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
-        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, vp]
-        L.fa_fwd.restype = i32
-        L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
-        L.fa_fwd_ex.restype = i32
-        L.fa_decode_split_ex.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32, i32, vp]
-        L.fa_decode_split_ex.restype = i32
-        L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, f32, vp]
-        L.fa_fwd_fp8.restype = i32
-        L.fa_decode_split_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32,
-                                            vp]
-        L.fa_decode_split_fp8kv.restype = i32
-        L.fa_decode_workspace_bytes.argtypes = [i64, i64, i64, i32]
-        L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
-        L.fa_decode_split.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, f32, i32, i32, vp]
-        L.fa_decode_split.restype = i32
-        L.fa_decode_combine.argtypes = [vp, ctypes.c_size_t, vp, vp, i64, i64, i64, i32, i32, vp]
-        L.fa_decode_combine.restype = i32
-        L.fa_fwd_masked_workspace_bytes.argtypes = [i64, i64]
-        L.fa_fwd_masked_workspace_bytes.restype = ctypes.c_size_t
-        L.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, ctypes.c_size_t, f32,
-                                    i32, vp]
-        L.fa_fwd_masked.restype = i32
-        L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
-        L.fa_decode_noalloc.restype = i32
-        L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
-        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, i64, i32,
-                             f32, i32, vp]
-        L.fa_bwd.restype = i32
-        L.fa_status_string.argtypes = [i32]
-        L.fa_status_string.restype = ctypes.c_char_p
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Opens a build of the library at `path` and declares its entry points (the functions of this
+    module call whichever library lib() returns).  Raises if the file does not exist."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m exact_attention_126_amd.build`")
+    L = ctypes.CDLL(path)
+    i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, vp]
+    L.fa_fwd.restype = i32
+    L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
+    L.fa_fwd_ex.restype = i32
+    L.fa_decode_split_ex.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_decode_split_ex.restype = i32
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, f32, vp]
+    L.fa_fwd_fp8.restype = i32
+    L.fa_decode_split_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, f32, i32,
+                                        vp]
+    L.fa_decode_split_fp8kv.restype = i32
+    L.fa_decode_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_decode_split.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_decode_split.restype = i32
+    L.fa_decode_combine.argtypes = [vp, ctypes.c_size_t, vp, vp, i64, i64, i64, i32, i32, vp]
+    L.fa_decode_combine.restype = i32
+    L.fa_fwd_masked_workspace_bytes.argtypes = [i64, i64]
+    L.fa_fwd_masked_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, ctypes.c_size_t, f32,
+                                i32, vp]
+    L.fa_fwd_masked.restype = i32
+    L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_decode_noalloc.restype = i32
+    L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, i64, i32,
+                         f32, i32, vp]
+    L.fa_bwd.restype = i32
+    L.fa_status_string.argtypes = [i32]
+    L.fa_status_string.restype = ctypes.c_char_p
+    return L
 
 
 def fa_status_string(status: int) -> str:

@@ -27,6 +27,9 @@ SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bw
 # that accumulates in VGPRs (otherwise every tile's S and dP are copied out of the AGPRs).
 SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CALIB_LIB = os.path.join(PKG, "libfa_calib.so")
+# The same sources built with FA_DEBUG_POISON_LDS=1 (retired LDS ring slots overwritten with NaN
+# before they are refilled); a test checks that it gives the normal library's outputs bit for bit.
+POISON_LIB = os.path.join(PKG, "libfa_poison.so")
 CALIB_SOURCES = ["calib_mfma.hip"]
 
 
@@ -55,15 +58,15 @@ def _run(cmd, verbose: bool, cwd=None):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, save_temps: bool = False, out: str = LIB, sources=None) -> str:
-    """Compiles every source to an object (in parallel, each with its own options), then links."""
+def build(verbose: bool = False, save_temps: bool = False, out: str = LIB, sources=None, extra=()) -> str:
+    """Compiles every source to an object (in parallel, each with its own options and extra), then links."""
     names = sources or SOURCES
     objdir = tempfile.mkdtemp(prefix="fa_build_")
     fd, tmp = tempfile.mkstemp(suffix=".so.tmp", dir=os.path.dirname(out))
     os.close(fd)
     try:
         objs = [os.path.join(objdir, n + ".o") for n in names]
-        cmds = [[hipcc(), *flags(save_temps), *SOURCE_FLAGS.get(n, []), "-c", "-o", o, os.path.join(CSRC, n)]
+        cmds = [[hipcc(), *flags(save_temps), *SOURCE_FLAGS.get(n, []), *extra, "-c", "-o", o, os.path.join(CSRC, n)]
                 for n, o in zip(names, objs)]
         workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0")) or len(os.sched_getaffinity(0))))
         with ThreadPoolExecutor(max_workers=workers) as ex:
@@ -86,6 +89,11 @@ def build_calib(verbose: bool = False) -> str:
     return build(verbose=verbose, out=CALIB_LIB, sources=CALIB_SOURCES)
 
 
+def build_poison(verbose: bool = False) -> str:
+    return build(verbose=verbose, out=POISON_LIB, extra=("-DFA_DEBUG_POISON_LDS=1",))
+
+
 if __name__ == "__main__":
     build(verbose=True, save_temps="--save-temps" in sys.argv)
     build_calib(verbose=True)
+    build_poison(verbose=True)

@@ -168,7 +168,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // only tiles past the wave's diagonal or the end of the keys are masked element by element.
   auto tile = [&](int t, auto slot) {
     constexpr int cur = decltype(slot)::value;
-    if (t + 1 < n) issue(t + 1, cur ^ 1);
+    if (t + 1 < n) {
+#if FA_DEBUG_POISON_LDS
+      {  // the slot of tile t - 1, retired by the last barrier
+#pragma unroll
+        for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+          const int x = wave + C::WAVES * i;
+          if (x < 2 * C::DMAS) {
+            const int c = x < C::DMAS ? x : x - C::DMAS;
+            poison16((FA_LDS char*)((x < C::DMAS ? kb[cur ^ 1] : vb[cur ^ 1]) + c * 1024 + lane * 16), kPoisonBf16);
+          }
+        }
+        poison_done();
+      }
+#endif
+      issue(t + 1, cur ^ 1);
+    }
     const FA_LDS char* kt = (const FA_LDS char*)kb[cur];
     const FA_LDS char* vt = (const FA_LDS char*)vb[cur];
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
@@ -519,7 +534,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       constexpr int p = decltype(P)::value;
       wait_loads_but(std::integral_constant<int, 0>{});
       bar();
-      if (k + 2 < n_steps) issue(tile_of(k + 2), std::integral_constant<int, (p + 2) % C::SLOTS>{});
+      if (k + 2 < n_steps) {
+        constexpr std::integral_constant<int, (p + 2) % C::SLOTS> SL{};
+#if FA_DEBUG_POISON_LDS
+        {  // the slot of tile k - 1, retired by this barrier
+#pragma unroll
+          for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+            const int x = wave + C::WAVES * i;
+            poison16((FA_LDS char*)((x < C::DMAS ? qslot(SL) : oslot(SL)) + (x % C::DMAS) * 1024 + lane * 16), kPoisonBf16);
+          }
+          if (wave == C::WAVES - 1) *((FA_LDS uint32_t*)sslot(SL) + lane) = kPoisonF32;
+          poison_done();
+        }
+#endif
+        issue(tile_of(k + 2), SL);
+      }
       // a tile that reaches past the wave's diagonal or the end of the queries: its masked
       // scores become -inf, so that P and dS are 0 there
       const int q0 = tile_of(k) * C::BQ;

@@ -67,6 +67,22 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 __device__ __forceinline__ u32x4_t lds_load16(const FA_LDS char* p) { return *(const FA_LDS u32x4_t*)p; }
 __device__ __forceinline__ void lds_store16(FA_LDS char* p, u32x4_t v) { *(FA_LDS u32x4_t*)p = v; }
 
+// Debug aid, off by default: built with FA_DEBUG_POISON_LDS=1, the waves that refill a slot of an
+// LDS tile ring first overwrite their share of it with NaN, after the barrier that retires the
+// slot and before their tile loads are issued.  With the barriers right no wave ever reads the
+// NaN (the loads overwrite it first), so such a build gives bit for bit the outputs of the normal
+// one; a missing or misplaced barrier would let a wave read the poison and turn its rows of O
+// into NaN.
+#ifndef FA_DEBUG_POISON_LDS
+#define FA_DEBUG_POISON_LDS 0
+#endif
+constexpr uint32_t kPoisonBf16 = 0x7FC07FC0u;  // two bf16 NaNs
+constexpr uint32_t kPoisonF32 = 0x7FC00000u;   // fp32 NaN
+constexpr uint32_t kPoisonE4M3 = 0x7F7F7F7Fu;  // four OCP E4M3 NaNs
+__device__ __forceinline__ void poison16(FA_LDS char* p, uint32_t w) { lds_store16(p, u32x4_t{w, w, w, w}); }
+// waits for this wave's poison stores, so that they land before the tile loads that follow
+__device__ __forceinline__ void poison_done() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
 // receives element (i % 4) of the 8-byte rows addressed by lanes 4e + i/4, e = 0..3.
 __device__ __forceinline__ i16x4_t lds_load8_tr16(const FA_LDS char* p) {

@@ -343,6 +343,16 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
         frag[i % (L + 1)] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
+#if FA_DEBUG_POISON_LDS
+    if constexpr (NDMA > 0) {  // the slots K_(j+1) and V_j are loaded into are retired
+#pragma unroll
+      for (int d = 0; d < C::DMA_PER_WAVE; ++d) {
+        poison16((FA_LDS char*)(kdst + (lw * C::DMA_PER_WAVE + d) * 1024 + lane * 16), kPoisonBf16);
+        poison16((FA_LDS char*)(vdst + (lw * C::DMA_PER_WAVE + d) * 1024 + lane * 16), kPoisonBf16);
+      }
+      poison_done();
+    }
+#endif
     s0 = f32x16_t{};
     s1 = f32x16_t{};
     static_for<L>([&](auto I) { read(I); });

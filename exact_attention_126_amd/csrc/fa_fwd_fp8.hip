@@ -244,6 +244,16 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
       else
         frag[i % (L + 1)] = vfrag(vt, i - NS);
     };
+#if FA_DEBUG_POISON_LDS
+    if constexpr (NDMA > 0) {  // the slots K_(j+1) and V_j are loaded into are retired
+#pragma unroll
+      for (int d = 0; d < C::DMA_PER_WAVE; ++d) {
+        poison16((FA_LDS char*)(kdst + (lw * C::DMA_PER_WAVE + d) * 1024 + lane * 16), kPoisonE4M3);
+        poison16((FA_LDS char*)(vdst + (lw * C::DMA_PER_WAVE + d) * 1024 + lane * 16), kPoisonE4M3);
+      }
+      poison_done();
+    }
+#endif
     s0 = f32x16_t{};
     s1 = f32x16_t{};
     static_for<L>([&](auto I) { read(I); });

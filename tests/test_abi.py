@@ -315,3 +315,21 @@ def test_bwd_validation(L):
     assert bwd(L, B=2**12, H=2**12, H_kv=2**12, Nq=2**10, wsb=1 << 40) == 3  # workspace offsets beyond 32 bits
     assert bwd(L, wsb=fa.fa_bwd_workspace_bytes(1, 4, 128) - 4) == 5
     assert bwd(L) in (0, 6)  # valid: with no GPU in this process the launch reports FA_ERR_HIP
+
+
+def test_poisoned_build_loads_and_exports_the_same_abi():
+    """libfa_poison.so (the FA_DEBUG_POISON_LDS=1 build) exports every declared entry point, and
+    its argument checks answer like the normal library's without launching."""
+    from exact_attention_126_amd import build as fa_build
+    if not os.path.exists(fa_build.POISON_LIB):
+        pytest.fail("libfa_poison.so is not built (python -m exact_attention_126_amd.build)")
+    out = subprocess.run(["nm", "-D", "--defined-only", fa_build.POISON_LIB], capture_output=True,
+                         text=True).stdout
+    assert set(_declared()) <= set(re.findall(r"\sT\s(fa_\w+)$", out, re.M))
+    Lp = fa.load_library(fa_build.POISON_LIB)
+    i64 = ctypes.c_int64
+    for args in ((None, P, P, P, P, 1, 2, 64, 64, 128, BF16, 0.1, 1, None),   # null q
+                 (P, P, P, P, P, 1, 2, 64, 64, 96, BF16, 0.1, 1, None),       # unsupported head dim
+                 (P_MIS, P, P, P, P, 1, 2, 64, 64, 128, BF16, 0.1, 1, None)):  # misaligned q
+        assert Lp.fa_fwd(*args) == fa.lib().fa_fwd(*args) != fa.FA_OK
+    assert Lp.fa_bwd_workspace_bytes(i64(2), i64(3), i64(100)) == fa.lib().fa_bwd_workspace_bytes(2, 3, 100)
