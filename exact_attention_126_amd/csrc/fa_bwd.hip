@@ -9,10 +9,11 @@
 //
 // Three kernels, all on one stream, with no atomics (the result is bit-reproducible):
 //  * bwd_pre_kernel: Dr and LSE in log2 units per query row, into the caller's workspace.
-//  * bwd_dq_kernel: query-major like the forward.  Each wave owns 32 queries and streams 32-key
-//    K/V tiles through LDS (LDS DMA, double buffered): S^T = K Q^T and dP^T = V dO^T on
+//  * bwd_dq_kernel: query-major and ping-pong like the forward.  Each wave owns 32 queries and
+//    streams 32-key K/V tiles through LDS rings (LDS DMA): S^T = K Q^T and dP^T = V dO^T on
 //    v_mfma_f32_32x32x16_bf16 with Q^T and dO^T held in VGPRs, then dS^T in VGPRs, then
-//    dQ^T += K^T dS^T with K^T read from LDS by the transposing ds_read_b64_tr_b16.  The
+//    dQ^T += K^T dS^T with K^T read from LDS by the transposing ds_read_b64_tr_b16.  Two groups of
+//    four waves alternate: while one issues a tile's products, the other computes its dS.  The
 //    accumulator-to-B-operand key order (key_of_row) is the forward's.
 //  * bwd_dkdv_kernel: key-major, the mirror image of bwd_dq_kernel.  Each wave (one per SIMD)
 //    owns 32 keys, with their K^T and V^T fragments in VGPRs, and streams 32-query tiles of Q,
@@ -63,9 +64,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------ dQ
+// Query-major, ping-pong like the forward: eight waves in two groups of four, each SIMD running
+// one wave of each group.  Workgroup barriers cut time into half-periods; in each, one group
+// issues the matrix products of a tile while the other turns its S and dP into dS on the VALU.
+// Per 32-key tile t and wave (32 queries):
+//   MFMA phase t: S_t^T = K_t Q^T and dP_t^T = V_t dO^T, then dQ^T += K_{t-1}^T dS_{t-1}^T, with
+//                 the A operands read from LDS a few MFMAs ahead;
+//   VALU phase t: dS_t^T = P_t^T * (dP_t^T - Dr), P = exp2(S sl2 - L2), packed to bf16.
+// Group g runs MFMA phase t in half-period 2t + g and VALU phase t in 2t + g + 1.  K_t is read
+// in four half-periods (as rows for S by both groups, then transposed for dQ by both) and V_t in
+// two, so K tiles sit in a four-slot ring and V tiles in a two-slot ring; group 0 loads tile t + 1
+// inside its MFMA phase t, two half-periods before its first use.
 template <int D>
 struct DqCfg {
-  static constexpr int WAVES = 8;
+  static constexpr int WAVES = 8;  // two groups of four, one wave of each per SIMD
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BR = WAVES * 32;  // queries per workgroup
   static constexpr int BC = 32;          // keys per tile
@@ -73,11 +85,19 @@ struct DqCfg {
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int TILE_BYTES = BC * RB;
   static constexpr int ROWS_PER_DMA = 64 / CPR;
-  static constexpr int DMAS = TILE_BYTES / 1024;                  // per tensor and tile
-  static constexpr int DMA_PER_WAVE = (2 * DMAS + WAVES - 1) / WAVES;  // K and V together
+  static constexpr int DMAS = TILE_BYTES / 1024;           // per tensor and tile
+  static constexpr int LOADERS = 4;                        // the waves of group 0 move the tiles
+  static constexpr int DMA_PER_WAVE = 2 * DMAS / LOADERS;  // K and V together
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
+  static constexpr int NS = 2 * KSTEPS;  // S and dP MFMAs per tile
+  static constexpr int N = NS + 2 * DBLK;  // and the dQ MFMAs
+  static_assert(DMAS % LOADERS == 0, "each loading wave moves whole K and V parts");
 };
+
+#ifndef FA_DQ_LOOKAHEAD
+#define FA_DQ_LOOKAHEAD 6  // MFMAs by which the dQ kernel's LDS operand reads run ahead
+#endif
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
@@ -85,8 +105,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dr,
     uint16_t* __restrict__ dQ, int H, int group, int Nq, int Nk, int n_qblk, float scale, float sl2, int diag) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char kb[2][C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb[2][C::TILE_BYTES];
+  // One array per ring slot, so that the compiler sees the loads into one slot never alias the
+  // reads of another.
+  __shared__ __attribute__((aligned(1024))) char k0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k2[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k3[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[C::TILE_BYTES];
+  auto kslot = [&](auto I) -> char* {
+    constexpr int i = decltype(I)::value % 4;
+    if constexpr (i == 0) return k0;
+    else if constexpr (i == 1) return k1;
+    else if constexpr (i == 2) return k2;
+    else return k3;
+  };
+  auto vslot = [&](auto I) -> char* {
+    if constexpr (decltype(I)::value % 2 == 0) return v0;
+    else return v1;
+  };
 
   // heaviest query blocks first (causal), each head's blocks together
   const int item = xcd_item();
@@ -97,6 +134,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* Vh = V + (int64_t)kvh * Nk * D;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
   const int q_wave0 = qblk * C::BR + wave * 32;
   const int q = q_wave0 + l32;
   const int qc = min(q, Nq - 1);
@@ -118,24 +156,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kv_end = CAUSAL ? min(Nk, qblk * C::BR + C::BR + diag) : Nk;
   const int n = (kv_end + C::BC - 1) / C::BC;
 
-  // tile loads: instruction x of a tile moves 1 KiB of K (x < DMAS) or V; lane L lands in row
-  // L / CPR, slot L % CPR of the instruction's rows and fetches the chunk the swizzle puts there
+  // Load d (0 <= d < DMA_PER_WAVE) of a loading wave for tile t: the first half of its loads move
+  // parts of K, the second half the same parts of V; lane L lands in row L / CPR, slot L % CPR of
+  // the part's rows and fetches the chunk the swizzle puts there.  A tile past the last (the load
+  // that runs ahead of the block's end) reloads the last one, harmlessly, into a free slot.
   const __amdgpu_buffer_rsrc_t Kr = raw_rsrc(Kh, Nk * C::RB), Vr = raw_rsrc(Vh, Nk * C::RB);
-  auto issue = [&](int t, int buf) {
-#pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      const int x = wave + C::WAVES * i;
-      if (x < 2 * C::DMAS) {
-        const int c = x < C::DMAS ? x : x - C::DMAS;
-        const int row = c * C::ROWS_PER_DMA + lane / C::CPR;
-        const uint32_t off =
-            (uint32_t)min(t * C::BC + row, Nk - 1) * C::RB + (((lane % C::CPR) ^ swz<D>(row)) << 4);
-        if (x < C::DMAS)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(Kr, (lptr_t)(kb[buf] + c * 1024), 16, off, 0, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(Vr, (lptr_t)(vb[buf] + c * 1024), 16, off, 0, 0, 0);
-      }
-    }
+  auto issue_one = [&](int t, int d, char* kdst, char* vdst) {
+    constexpr int HALF = C::DMA_PER_WAVE / 2;
+    const int c = wave + C::LOADERS * (d % HALF);
+    const int row = c * C::ROWS_PER_DMA + lane / C::CPR;
+    const int tt = min(t, n - 1);
+    const uint32_t off = (uint32_t)min(tt * C::BC + row, Nk - 1) * C::RB + (((lane % C::CPR) ^ swz<D>(row)) << 4);
+    char* dst = (d < HALF ? kdst : vdst) + c * 1024;
+#if FA_DEBUG_POISON_LDS
+    poison16((FA_LDS char*)(dst + lane * 16), kPoisonBf16);
+    poison_done();
+#endif
+    if (d < HALF)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Kr, (lptr_t)dst, 16, off, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Vr, (lptr_t)dst, 16, off, 0, 0, 0);
   };
 
   // per-lane LDS offsets: 16-byte row reads of permuted keys (A of S^T and dP^T) and transposing
@@ -163,39 +203,74 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16_t dq[C::DBLK];
 #pragma unroll
   for (int mb = 0; mb < C::DBLK; ++mb) dq[mb] = f32x16_t{};
+  f32x16_t s = f32x16_t{}, dp = f32x16_t{};  // S^T and dP^T of the wave's current tile
+  u32x4_t dsb[2];                             // bf16 dS^T of the previous tile, two 16-key groups
 
-  // One 32-key tile with its LDS slot fixed at compile time (the loop below alternates the two);
-  // only tiles past the wave's diagonal or the end of the keys are masked element by element.
-  auto tile = [&](int t, auto slot) {
-    constexpr int cur = decltype(slot)::value;
-    if (t + 1 < n) {
-#if FA_DEBUG_POISON_LDS
-      {  // the slot of tile t - 1, retired by the last barrier
-#pragma unroll
-        for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-          const int x = wave + C::WAVES * i;
-          if (x < 2 * C::DMAS) {
-            const int c = x < C::DMAS ? x : x - C::DMAS;
-            poison16((FA_LDS char*)((x < C::DMAS ? kb[cur ^ 1] : vb[cur ^ 1]) + c * 1024 + lane * 16), kPoisonBf16);
-          }
-        }
-        poison_done();
+  // MFMA phase t with K_t in K slot KS (K_{t-1} in KS - 1) and V_t in V slot VS: the S / dP
+  // products (DO_S) and dQ of tile t - 1 (DO_DQ), written as an explicit pipeline: slot i issues
+  // MFMA i, then the LDS reads of the A operand of MFMA i + L into a rotating set of L + 1
+  // registers, and (group 0, LOAD) every few slots one load of tile t + 1 into K slot KS + 1 and
+  // V slot VS + 1.  Scheduling barriers between the slots keep the read-ahead.
+  auto mfma_phase = [&](int t, auto KSc, auto VSc, auto DO_S, auto DO_DQ, auto LOAD, const char* kprev) {
+    constexpr int KS = decltype(KSc)::value, VS = decltype(VSc)::value;
+    constexpr int L = FA_DQ_LOOKAHEAD;
+    constexpr int i0 = decltype(DO_S)::value ? 0 : C::NS, i1 = decltype(DO_DQ)::value ? C::N : C::NS;
+    constexpr int NDMA = decltype(LOAD)::value ? C::DMA_PER_WAVE : 0;
+    constexpr int EVERY = (i1 - i0) / (NDMA > 0 ? NDMA : 1);
+    const FA_LDS char* kt = (const FA_LDS char*)kslot(std::integral_constant<int, KS>{});
+    const FA_LDS char* vt = (const FA_LDS char*)vslot(std::integral_constant<int, VS>{});
+    const FA_LDS char* kp = (const FA_LDS char*)kprev;  // K_{t-1}
+    char* kdst = kslot(std::integral_constant<int, KS + 1>{});
+    char* vdst = vslot(std::integral_constant<int, VS + 1>{});
+    bf16x8_t fr[L + 1];
+    auto read = [&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < C::NS) {
+        fr[i % (L + 1)] = as_bf16x8(lds_load16(((i & 1) ? vt : kt) + koff[i >> 1]));
+      } else {
+        constexpr int c = i - C::NS, t2 = c / C::DBLK, mb = c % C::DBLK;
+        const i16x4_t lo = lds_load8_tr16(kp + toff[mb][0] + t2 * 16 * C::RB);
+        const i16x4_t hi = lds_load8_tr16(kp + toff[mb][1] + t2 * 16 * C::RB);
+        fr[i % (L + 1)] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-#endif
-      issue(t + 1, cur ^ 1);
+    };
+    if constexpr (decltype(DO_S)::value) {
+      s = f32x16_t{};
+      dp = f32x16_t{};
     }
-    const FA_LDS char* kt = (const FA_LDS char*)kb[cur];
-    const FA_LDS char* vt = (const FA_LDS char*)vb[cur];
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    static_for<L>([&](auto I) {
+      if constexpr (i0 + decltype(I)::value < i1) read(std::integral_constant<int, i0 + decltype(I)::value>{});
+    });
+    static_for<C::N>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i >= i0 && i < i1) {
+        if constexpr (i < C::NS) {
+          if constexpr (i & 1)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (L + 1)], dof[i >> 1], dp, 0, 0, 0);
+          else
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (L + 1)], qf[i >> 1], s, 0, 0, 0);
+        } else {
+          constexpr int c = i - C::NS, t2 = c / C::DBLK, mb = c % C::DBLK;
+          dq[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (L + 1)], as_bf16x8(dsb[t2]), dq[mb], 0, 0, 0);
+        }
+        if constexpr (i + L < i1) read(std::integral_constant<int, i + L>{});
+        if constexpr (NDMA > 0 && (i - i0) % EVERY == 0 && (i - i0) / EVERY < NDMA)
+          issue_one(t + 1, (i - i0) / EVERY, kdst, vdst);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+    // keep the products in this phase (the next phase would otherwise absorb them)
+    asm volatile("" : "+v"(s), "+v"(dp));
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_load16(kt + koff[ks])), qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_load16(vt + koff[ks])), dof[ks], dp, 0, 0, 0);
-    }
-    // P^T and dS^T; register j of lane-half hh holds key 16 (j / 8) + 8 hh + j % 8 of the tile
+    for (int mb = 0; mb < C::DBLK; ++mb) asm volatile("" : "+v"(dq[mb]));
+  };
+
+  // VALU phase t: P^T and dS^T of the wave's tile; register j of lane-half hh holds key
+  // 16 (j / 8) + 8 hh + j % 8 of the tile.  Only tiles past the wave's diagonal or the end of the
+  // keys are masked element by element.
+  auto valu_phase = [&](int t) {
     const int tile0 = t * C::BC;
     const bool need_mask = (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag);
-    u32x4_t dsb[2];
     auto ds_tile = [&](auto mask_tag) {
       const int lim = CAUSAL ? min(Nk - 1, q + diag) : Nk - 1;
 #pragma unroll
@@ -219,29 +294,88 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ds_tile(std::true_type{});
     else
       ds_tile(std::false_type{});
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int mb = 0; mb < C::DBLK; ++mb) {
-        const i16x4_t lo = lds_load8_tr16(kt + toff[mb][0] + t2 * 16 * C::RB);
-        const i16x4_t hi = lds_load8_tr16(kt + toff[mb][1] + t2 * 16 * C::RB);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        dq[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(dsb[t2]), dq[mb], 0, 0, 0);
-      }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
-    __syncthreads();                     // ... for every wave, and this tile's reads are done
+    asm volatile("" : "+v"(dsb[0]), "+v"(dsb[1]));
   };
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  int t = 0;
-  for (; t + 1 < n; t += 2) {
-    tile(t, std::integral_constant<int, 0>{});
-    tile(t + 1, std::integral_constant<int, 1>{});
+  auto bar = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  constexpr std::true_type Y{};
+  constexpr std::false_type F{};
+  constexpr std::integral_constant<int, 0> I0{};
+  constexpr std::integral_constant<int, 1> I1{};
+  constexpr std::integral_constant<int, 2> I2{};
+  constexpr std::integral_constant<int, 3> I3{};
+  // K slot of tile KS - 1
+  auto kprev = [&](auto KSc) -> const char* { return kslot(std::integral_constant<int, decltype(KSc)::value + 3>{}); };
+  // the last MFMA phase (tile n: dQ of tile n - 1 only), with K_{n-1} in K slot (n - 1) mod 4
+  auto last_dq = [&]() {
+    const int r = (n - 1) & 3;
+    const char* kl = r == 0 ? k0 : r == 1 ? k1 : r == 2 ? k2 : k3;
+    mfma_phase(n, I0, I0, F, Y, F, kl);
+  };
+
+  if (grp == 0) {
+#pragma unroll
+    for (int d = 0; d < C::DMA_PER_WAVE; ++d) issue_one(0, d, k0, v0);
   }
-  if (t < n) tile(t, std::integral_constant<int, 0>{});
+  wait_loads();
+  bar();
+  if (grp == 0) {
+    mfma_phase(0, I0, I0, Y, F, Y, k3);  // h = 0: S_0, dP_0; loads tile 1
+    bar();
+    valu_phase(0);  // h = 1
+    wait_loads();
+    bar();
+    // tile t: MFMA phase in half-period 2t, VALU phase in 2t + 1
+    auto both = [&](int t, auto KSc, auto VSc) {
+      mfma_phase(t, KSc, VSc, Y, Y, Y, kprev(KSc));
+      bar();
+      valu_phase(t);
+      wait_loads();
+      bar();
+    };
+    int t = 1;
+    for (; t + 3 < n; t += 4) {
+      both(t, I1, I1);
+      both(t + 1, I2, I0);
+      both(t + 2, I3, I1);
+      both(t + 3, I0, I0);
+    }
+    if (t < n) both(t, I1, I1);
+    if (t + 1 < n) both(t + 1, I2, I0);
+    if (t + 2 < n) both(t + 2, I3, I1);
+    last_dq();  // h = 2n
+    bar();
+  } else {
+    bar();                           // h = 0: idle
+    mfma_phase(0, I0, I0, Y, F, F, k3);  // h = 1
+    bar();
+    // tile t: VALU phase of tile t - 1 in half-period 2t, MFMA phase of tile t in 2t + 1
+    auto both = [&](int t, auto KSc, auto VSc) {
+      valu_phase(t - 1);
+      bar();
+      mfma_phase(t, KSc, VSc, Y, Y, F, kprev(KSc));
+      bar();
+    };
+    int t = 1;
+    for (; t + 3 < n; t += 4) {
+      both(t, I1, I1);
+      both(t + 1, I2, I0);
+      both(t + 2, I3, I1);
+      both(t + 3, I0, I0);
+    }
+    if (t < n) both(t, I1, I1);
+    if (t + 1 < n) both(t + 1, I2, I0);
+    if (t + 2 < n) both(t + 2, I3, I1);
+    valu_phase(n - 1);  // h = 2n
+    bar();
+    last_dq();  // h = 2n + 1
+  }
 
   if (q < Nq) {
     uint16_t* op = dQ + ((int64_t)bh * Nq + q) * D + 4 * hh;
