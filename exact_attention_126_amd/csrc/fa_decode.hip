@@ -269,10 +269,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
 //    the wave's own, and its A operand (dim 16 mb + l % 16 of those same eight keys) comes from
 //    two transposing ds_read_b64_tr_b16 reads.  O^T's lane l holds query l % 16, so the rescale by
 //    exp2(m_old - m_new) is a per-lane scalar.
-// Rows of the V buffers are XOR-swizzled in 16-byte chunks by the row's low bits.  K registers and
-// V buffers are double-buffered, so each wave has its next trip's rows in flight while it computes
-// the current one (its K rows from the trip's start, its V rows from the trip's PV products on).  The four waves merge their states through LDS as in the kernel above and write
-// the same partials.
+// Rows of the V buffers are XOR-swizzled in 16-byte chunks by the row's low bits.  Each wave loads
+// one trip at a time (its K rows into registers, its V rows into its buffer) and computes it; three
+// workgroups per compute unit keep other waves' loads in flight meanwhile.  The four waves merge
+// their states through LDS as in the kernel above and write the same partials.
 #ifndef FA_DEC_TRIP
 #define FA_DEC_TRIP 32  // keys per wave per trip of the matrix-core decode split
 #endif
