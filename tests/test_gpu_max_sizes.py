@@ -6,6 +6,7 @@
 * fa_fwd_ex, bottom-right causal: a ragged chunk of queries against a long cache of 200003 keys
   (the last key tile partial, the diagonal offset 199703).
 * fa_decode_split + fa_decode_combine over 262144 cached keys in 128 splits.
+* fa_bwd for the same kind of chunk against 65537 keys, with grouped heads.
 Each case runs at a few heads, so the oracle takes seconds.
 """
 from __future__ import annotations
@@ -109,3 +110,17 @@ def test_decode_long_cache_many_splits():
     f = {x: si.as_f32(w, host[x]) for x in "qkv"}
     o_ref, l_ref = oracle.attention(f["q"], f["k"], f["v"], w.scale)
     assert_parity("bf16", metrics(from_device(o), from_device(lse).reshape(l_ref.shape), o_ref, l_ref), w.name)
+
+
+def test_bwd_chunk_against_long_cache():
+    """fa_bwd for a bottom-right chunk of 300 queries against 65537 keys (the last key tile
+    partial), grouped heads, against the reference and the per-element bounds."""
+    from tests import bwd_bounds
+    from tests.test_gpu_bwd import _inputs as bwd_inputs, _run as bwd_run, _w as bwd_w
+    w = bwd_w("bwd_nq300_nk65537_br_g2", 1, 4, 2, 300, 65537, 128, "bottom_right", seed=206)
+    host, dev = bwd_inputs(w)
+    (dq, dk, dv), (o, lse) = bwd_run(w, dev, with_forward=True)
+    f = {x: si.as_f32(w, host[x]) for x in host}
+    res = bwd_bounds.reference_and_bounds(f["q"], f["k"], f["v"], f["do"], from_device(o), from_device(lse), w.scale,
+                                          w.causal, w.diag)
+    bwd_bounds.check({"dq": from_device(dq), "dk": from_device(dk), "dv": from_device(dv)}, res, w.name)
