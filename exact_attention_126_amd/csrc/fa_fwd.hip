@@ -57,12 +57,14 @@
 namespace fa {
 namespace {
 
-template <int D>
+template <int D, int BCK = 64>
 struct Bf16Cfg {
   static constexpr int WAVES = 8;        // two groups of four, one wave of each per SIMD
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BR = WAVES * 32;  // query rows per workgroup, 32 per wave
-  static constexpr int BC = 64;          // keys per tile
+  static constexpr int BC = BCK;         // keys per tile
+  static constexpr int SB = BC / 32;     // 32-key blocks of S^T per tile
+  static constexpr int PG = BC / 16;     // 16-key groups of P^T per tile (k-steps of O^T += V^T P^T)
   static constexpr int RB = D * 2;       // bytes per LDS row
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int TILE_BYTES = BC * RB;
@@ -94,6 +96,15 @@ struct MaskView {
 // O_acc rescale.  Exponentials are then bounded by 2^kLazyRescale (exact: softmax does not
 // depend on the value subtracted, Day-21 page §5.2).
 constexpr float kLazyRescale = 8.f;
+
+#ifndef FA_D64_TILE
+#define FA_D64_TILE 128  // keys per tile of the d = 64 forward without an element mask
+#endif
+// Keys per tile: 64, and FA_D64_TILE at d = 64 without an element mask (the tile classification of
+// the masked forward is per 64 keys).  A larger tile at d = 64 halves the barriers and the per-tile
+// work of the softmax (decision, tile loads) per key; at d = 128 its accumulators would not fit.
+template <int D, bool MASKED>
+constexpr int kTileKeys = (D == 64 && !MASKED) ? FA_D64_TILE : 64;
 
 #ifndef FA_LOOKAHEAD
 #define FA_LOOKAHEAD 8  // MFMAs by which LDS operand reads run ahead
@@ -127,7 +138,8 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
                                           int diag, int qblk, int n_qblk, char* kb0, char* kb1, char* vb0,
                                           char* vb1, char* stg, bf16x8_t (&qf)[Bf16Cfg<D>::KSTEPS], bool pre,
                                           bool has_next, int nbh, int nkvh, int nqblk, const MaskView& mk) {
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, kTileKeys<D, MASKED>>;
+  static_assert(!MASKED || C::BC == 64, "the mask classification lists 64-key tiles");
   const uint16_t* Kh = K + (int64_t)kvh * Nk * D;
   const uint16_t* Vh = V + (int64_t)kvh * Nk * D;
 
@@ -252,7 +264,9 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // largest exponential, summed (the same in both lane halves; it joins l only where O is
   // normalised, see softmax_phase).
   float m2 = -INFINITY, lsum = 0.f, csum = 0.f;
-  f32x16_t s0, s1;  // S^T of the current tile, two 32-key blocks
+  f32x16_t sacc[C::SB];  // S^T of the current tile, 32-key blocks
+  f32x16_t& s0 = sacc[0];
+  f32x16_t& s1 = sacc[1];
   // With a mask: the lane's row's 64-bit mask word for the tile whose softmax comes next, loaded
   // one softmax phase ahead (the one for the first tile before the loop).
   const uint64_t* mrow = nullptr;
@@ -261,26 +275,27 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     mrow = mk.words + (int64_t)min(q_wave0 + l32, Nq - 1) * mk.nT;
     mword = mrow[first_tile];
   }
-  u32x4_t pb[4];    // bf16 P^T of the previous tile, four 16-key groups
+  u32x4_t pb[C::PG];  // bf16 P^T of the previous tile, 16-key groups
 
   // S_j = K_j Q^T
   auto qk = [&](const char* kbuf) {
     const FA_LDS char* kt = (const FA_LDS char*)kbuf;
-    s0 = f32x16_t{};
-    s1 = f32x16_t{};
+#pragma unroll
+    for (int b = 0; b < C::SB; ++b) sacc[b] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      const bf16x8_t a0 = as_bf16x8(lds_load16(kt + koff[ks]));
-      const bf16x8_t a1 = as_bf16x8(lds_load16(kt + 32 * C::RB + koff[ks]));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+      bf16x8_t a[C::SB];
+#pragma unroll
+      for (int b = 0; b < C::SB; ++b) a[b] = as_bf16x8(lds_load16(kt + b * 32 * C::RB + koff[ks]));
+#pragma unroll
+      for (int b = 0; b < C::SB; ++b) sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[b], qf[ks], sacc[b], 0, 0, 0);
     }
   };
   // O^T += V^T P^T of the previous tile
   auto pv = [&](const char* vbuf) {
     const FA_LDS char* vt = (const FA_LDS char*)vbuf;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < C::PG; ++t)
 #pragma unroll
       for (int mb = 0; mb < C::DBLK; ++mb) {
         const i16x4_t lo = lds_load8_tr16(vt + voff[mb][0] + t * 16 * C::RB);
@@ -298,24 +313,42 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // the max stays in the softmax phase.
   constexpr bool EARLY_MAX = (D == 64);
   float smax_pre = 0.f, mxp = 0.f;
-  auto max_step = [&](auto St) {  // step St of the max chain over s0, s1
+  // step St of the max chain over the tile's 16 SB scores, CH steps: value f of the chain is
+  // register f / SB of block f % SB
+  constexpr int CH = 8 * C::SB;
+  auto max_step = [&](auto St) {
     constexpr int st = decltype(St)::value;
-    if constexpr (st == 0) mxp = max3f(s0[0], s0[1], s1[0]);
-    else if constexpr (st == 1) mxp = max3f(mxp, s1[1], s0[2]);
-    else if constexpr (st < 15) mxp = max3f(mxp, s1[st], s0[st + 1]);
-    else mxp = max3f(mxp, s1[15], s1[15]);
+    if constexpr (C::SB == 2) {
+      if constexpr (st == 0) mxp = max3f(s0[0], s0[1], s1[0]);
+      else if constexpr (st == 1) mxp = max3f(mxp, s1[1], s0[2]);
+      else if constexpr (st < 15) mxp = max3f(mxp, s1[st], s0[st + 1]);
+      else mxp = max3f(mxp, s1[15], s1[15]);
+    } else {
+      constexpr int NV = 16 * C::SB;
+      auto v = [&](auto F) -> float { constexpr int f = decltype(F)::value; return sacc[f % C::SB][f / C::SB]; };
+      if constexpr (st == 0) {
+        mxp = max3f(v(std::integral_constant<int, 0>{}), v(std::integral_constant<int, 1>{}),
+                    v(std::integral_constant<int, 2>{}));
+      } else {
+        constexpr int f1 = 2 * st + 1, f2 = (2 * st + 2 < NV) ? 2 * st + 2 : NV - 1;
+        mxp = max3f(mxp, v(std::integral_constant<int, f1>{}), v(std::integral_constant<int, f2>{}));
+      }
+    }
   };
   auto max_halves = [&](float x) {  // across the two lane halves, without fmaxf's canonicalising
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
   };
   auto row_max_now = [&]() {
-    static_for<16>([&](auto St) { max_step(St); });
+    static_for<CH>([&](auto St) { max_step(St); });
     smax_pre = max_halves(mxp);
   };
   // Pins the MFMA results to the phase that computes them (see the fence in softmax_phase).
   auto fence_acc = [&]() {
-    asm volatile("" : "+v"(s0), "+v"(s1));
+    if constexpr (C::SB == 2)
+      asm volatile("" : "+v"(s0), "+v"(s1));
+    else
+      asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]), "+v"(sacc[2]), "+v"(sacc[3]));
 #pragma unroll
     for (int mb = 0; mb < C::DBLK; ++mb) asm volatile("" : "+v"(oacc[mb]));
   };
@@ -326,7 +359,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // harmless reload of a valid tile when j + 1 = n) and V_j into the free slots kdst and vdst.  Scheduling
   // barriers between slots keep the compiler from collapsing the read-ahead.
   auto mfma_phase = [&](auto load_tag, int j, const char* kbuf, const char* vbuf, char* kdst, char* vdst) {
-    constexpr int NS = 2 * C::KSTEPS, NP = 4 * C::DBLK, N = NS + NP, L = FA_LOOKAHEAD;
+    constexpr int NS = C::SB * C::KSTEPS, NP = C::PG * C::DBLK, N = NS + NP, L = FA_LOOKAHEAD;
     constexpr int NDMA = decltype(load_tag)::value ? 2 * C::DMA_PER_WAVE : 0;
     constexpr int DMA_EVERY = N / (NDMA > 0 ? NDMA : 1);
     const FA_LDS char* kt = (const FA_LDS char*)kbuf;
@@ -335,7 +368,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     auto read = [&](auto I) {  // A operand of MFMA I
       constexpr int i = decltype(I)::value;
       if constexpr (i < NS) {
-        frag[i % (L + 1)] = as_bf16x8(lds_load16(kt + (i & 1) * 32 * C::RB + koff[i >> 1]));
+        frag[i % (L + 1)] = as_bf16x8(lds_load16(kt + (i % C::SB) * 32 * C::RB + koff[i / C::SB]));
       } else {
         constexpr int t = (i - NS) / C::DBLK, mb = (i - NS) % C::DBLK;
         const i16x4_t lo = lds_load8_tr16(vt + voff[mb][0] + t * 16 * C::RB);
@@ -353,28 +386,26 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
       poison_done();
     }
 #endif
-    s0 = f32x16_t{};
-    s1 = f32x16_t{};
+#pragma unroll
+    for (int b = 0; b < C::SB; ++b) sacc[b] = f32x16_t{};
     static_for<L>([&](auto I) { read(I); });
     static_for<N>([&](auto I) {
       constexpr int i = decltype(I)::value;
       if constexpr (i < NS) {
-        if constexpr (i & 1)
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % (L + 1)], qf[i >> 1], s1, 0, 0, 0);
-        else
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % (L + 1)], qf[i >> 1], s0, 0, 0, 0);
+        sacc[i % C::SB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % (L + 1)], qf[i / C::SB], sacc[i % C::SB], 0, 0, 0);
       } else {
         constexpr int t = (i - NS) / C::DBLK, mb = (i - NS) % C::DBLK;
         oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % (L + 1)], as_bf16x8(pb[t]), oacc[mb], 0, 0, 0);
       }
       if constexpr (i + L < N) read(std::integral_constant<int, i + L>{});
       // the max chain over this phase's S, from the second P V slot on (S is complete by then)
-      constexpr int SPS = (16 + (NP - 3)) / (NP - 2);  // steps per slot over slots NS + 1 .. N - 2
+      constexpr int SPS = (CH + (NP - 3)) / (NP - 2);  // steps per slot over slots NS + 1 .. N - 2
       if constexpr (EARLY_MAX && i >= NS + 1 && i <= N - 2) {
         constexpr int k0 = (i - NS - 1) * SPS;
         static_for<SPS>([&](auto T) {
           constexpr int st = k0 + decltype(T)::value;
-          if constexpr (st < 16) max_step(std::integral_constant<int, st>{});
+          if constexpr (st < CH) max_step(std::integral_constant<int, st>{});
         });
       }
       if constexpr (EARLY_MAX && i == N - 1) smax_pre = max_halves(mxp);
@@ -429,8 +460,9 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
           const int key = tile0 + 16 * (jj >> 3) + 8 * hh + (jj & 7);
-          if (key > lim) s0[jj] = -INFINITY;
-          if (key + 32 > lim) s1[jj] = -INFINITY;
+#pragma unroll
+          for (int b = 0; b < C::SB; ++b)
+            if (key + 32 * b > lim) sacc[b][jj] = -INFINITY;
         }
       }
     }
@@ -457,8 +489,8 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     }
     float rs;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const f32x16_t& s = (t < 2) ? s0 : s1;
+    for (int t = 0; t < C::PG; ++t) {
+      const f32x16_t& s = sacc[t >> 1];
       const int j0 = 8 * (t & 1);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -471,7 +503,12 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     lsum += rs;
     // Keep this phase's vector work in this phase: without the fence the compiler sinks the
     // exponentials past the barrier, next to their use in the other group's MFMA phase.
-    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum), "+v"(m2), "+v"(csum));
+    if constexpr (C::PG == 4) {
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum), "+v"(m2), "+v"(csum));
+    } else {
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum), "+v"(m2), "+v"(csum));
+      asm volatile("" : "+v"(pb[4]), "+v"(pb[5]), "+v"(pb[6]), "+v"(pb[7]));
+    }
     (void)mcur;
   };
 
@@ -620,7 +657,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int n_items, int items_per_head,
     int xcd_split, float sl2, int H, int group, int diag, int paired, const int* __restrict__ mcounts,
     const uint16_t* __restrict__ mlists, const uint64_t* __restrict__ mwords, int nT) {
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, kTileKeys<D, MASKED>>;
   static_assert(!(CAUSAL && MASKED), "a causal mask is one element mask among others");
   // LDS copy of the current block's tile list (masked forward only)
   __shared__ uint16_t tl[MASKED ? kMaxMaskTiles : 1];
