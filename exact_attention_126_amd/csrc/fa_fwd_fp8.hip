@@ -7,7 +7,7 @@
 // gfx950 mapping (what differs from the bf16 kernel):
 //  * Both products on v_mfma_f32_32x32x64_f8f6f4 (fp8 x fp8, fp32 accumulate), which does four
 //    times the k-depth of the bf16 32x32x16 in twice its cycles: S^T = K Q^T takes D/64 k-steps
-//    per 32-key block, O^T = V^T P^T one k-step per 64-key tile and 32-dim block.  Each operand
+//    per 32-key block, O^T = V^T P^T one k-step per 64 keys and 32-dim block.  Each operand
 //    lane holds 32 bytes (k values) of row or column l % 32; A and B share the k order, which is
 //    all the products need.
 //  * Codes multiply as codes: S^T is Q_codes K_codes^T, and scale * q_scale * k_scale * log2(e) is
@@ -35,12 +35,19 @@ namespace {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
-template <int D>
+#ifndef FA8_TILE
+#define FA8_TILE 128  // keys per tile: with 128 the MFMA phase (16 MFMAs at d = 128) is as long as the
+                      // bf16 kernel's, and the barriers and per-tile softmax work per key halve
+#endif
+
+template <int D, int BCK = FA8_TILE>
 struct Fp8Cfg {
   static constexpr int WAVES = 8;  // two groups of four, one wave of each per SIMD
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BR = WAVES * 32;  // query rows per workgroup, 32 per wave
-  static constexpr int BC = 64;          // keys per tile
+  static constexpr int BC = BCK;         // keys per tile
+  static constexpr int SB = BC / 32;     // 32-key blocks of S^T per tile
+  static constexpr int PH = BC / 64;     // 64-key k-steps of O^T += V^T P^T per tile
   static constexpr int RB = D;           // bytes per LDS row
   static constexpr int CPR = D / 16;     // 16-byte chunks per row
   static constexpr int TILE_BYTES = BC * RB;
@@ -73,7 +80,7 @@ __device__ __forceinline__ int swz8<64>(int row) {
   return ((row & 4) ? 1 : 0) ^ ((row & 8) ? 2 : 0);
 }
 
-// Key row (within a 64-key tile) of byte b (0..31) of the P operand in lane-half h: the
+// Key row (within 64 keys of the tile) of byte b (0..31) of the P operand in lane-half h: the
 // accumulator row of the S^T register it was converted from.
 __device__ __forceinline__ int key_of_pbyte(int b, int h) {
   const int blk = b >> 4, j = b & 15;
@@ -175,10 +182,15 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
 #pragma unroll
   for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] = f32x16_t{};
   float m2 = -INFINITY, lsum = 0.f;
-  f32x16_t s0, s1;  // S^T of the current tile, two 32-key blocks
-  // E4M3 P^T of the previous tile (32 keys per lane-half).  Zeroed once per block: the packing
-  // below reads each word (only to overwrite it half by half), so it must never be indeterminate.
-  i32x8_t pb = {};
+  f32x16_t sacc[C::SB];  // S^T of the current tile, 32-key blocks
+  f32x16_t& s0 = sacc[0];
+  f32x16_t& s1 = sacc[1];
+  // E4M3 P^T of the previous tile, per 64 keys (32 keys per lane-half).  Zeroed once per block:
+  // the packing below reads each word (only to overwrite it half by half), so it must never be
+  // indeterminate.
+  i32x8_t pb[C::PH];
+#pragma unroll
+  for (int h = 0; h < C::PH; ++h) pb[h] = i32x8_t{};
 
   auto kfrag = [&](const FA_LDS char* kt, int blk, int ks) {
     return join16(lds_load16(kt + blk * 32 * C::RB + koff[ks][0]), lds_load16(kt + blk * 32 * C::RB + koff[ks][1]));
@@ -190,18 +202,19 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
   };
   auto qk = [&](const char* kbuf) {
     const FA_LDS char* kt = (const FA_LDS char*)kbuf;
-    s0 = f32x16_t{};
-    s1 = f32x16_t{};
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      s0 = mfma8(kfrag(kt, 0, ks), qf[ks], s0);
-      s1 = mfma8(kfrag(kt, 1, ks), qf[ks], s1);
-    }
+    for (int b = 0; b < C::SB; ++b) sacc[b] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+      for (int b = 0; b < C::SB; ++b) sacc[b] = mfma8(kfrag(kt, b, ks), qf[ks], sacc[b]);
   };
   auto pv = [&](const char* vbuf) {
     const FA_LDS char* vt = (const FA_LDS char*)vbuf;
 #pragma unroll
-    for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] = mfma8(vfrag(vt, mb), pb, oacc[mb]);
+    for (int h = 0; h < C::PH; ++h)
+#pragma unroll
+      for (int mb = 0; mb < C::DBLK; ++mb) oacc[mb] = mfma8(vfrag(vt + h * 64 * C::RB, mb), pb[h], oacc[mb]);
   };
   // The tile's largest raw score of this lane's row is taken in the MFMA phase that computes S,
   // under its P V products (sixteen dependent max3 steps, then the swap across the lane halves):
@@ -209,29 +222,47 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
   // instruction only every few cycles.  Tiles that need an element mask take it again after
   // masking.
   float smax_pre = 0.f, mxp = 0.f;
-  auto max_step = [&](auto St) {  // step St of the max chain over s0, s1
+  // step St of the max chain over the tile's 16 SB scores, CH steps: value f of the chain is
+  // register f / SB of block f % SB
+  constexpr int CH = 8 * C::SB;
+  auto max_step = [&](auto St) {
     constexpr int st = decltype(St)::value;
-    if constexpr (st == 0) mxp = max3f(s0[0], s0[1], s1[0]);
-    else if constexpr (st == 1) mxp = max3f(mxp, s1[1], s0[2]);
-    else if constexpr (st < 15) mxp = max3f(mxp, s1[st], s0[st + 1]);
-    else mxp = max3f(mxp, s1[15], s1[15]);
+    if constexpr (C::SB == 2) {
+      if constexpr (st == 0) mxp = max3f(s0[0], s0[1], s1[0]);
+      else if constexpr (st == 1) mxp = max3f(mxp, s1[1], s0[2]);
+      else if constexpr (st < 15) mxp = max3f(mxp, s1[st], s0[st + 1]);
+      else mxp = max3f(mxp, s1[15], s1[15]);
+    } else {
+      constexpr int NV = 16 * C::SB;
+      auto v = [&](auto F) -> float { constexpr int f = decltype(F)::value; return sacc[f % C::SB][f / C::SB]; };
+      if constexpr (st == 0) {
+        mxp = max3f(v(std::integral_constant<int, 0>{}), v(std::integral_constant<int, 1>{}),
+                    v(std::integral_constant<int, 2>{}));
+      } else {
+        constexpr int f1 = 2 * st + 1, f2 = (2 * st + 2 < NV) ? 2 * st + 2 : NV - 1;
+        mxp = max3f(mxp, v(std::integral_constant<int, f1>{}), v(std::integral_constant<int, f2>{}));
+      }
+    }
   };
   auto max_halves = [&](float x) {  // across the two lane halves, without fmaxf's canonicalising
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
   };
   auto row_max_now = [&]() {
-    static_for<16>([&](auto St) { max_step(St); });
+    static_for<CH>([&](auto St) { max_step(St); });
     smax_pre = max_halves(mxp);
   };
   auto fence_acc = [&]() {
-    asm volatile("" : "+v"(s0), "+v"(s1));
+    if constexpr (C::SB == 2)
+      asm volatile("" : "+v"(s0), "+v"(s1));
+    else
+      asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]), "+v"(sacc[2]), "+v"(sacc[3]));
 #pragma unroll
     for (int mb = 0; mb < C::DBLK; ++mb) asm volatile("" : "+v"(oacc[mb]));
   };
   // MFMA phase j: S_j and O += P_{j-1} V_{j-1} as an explicit pipeline (see fa_fwd.hip).
   auto mfma_phase = [&](auto load_tag, int j, const char* kbuf, const char* vbuf, char* kdst, char* vdst) {
-    constexpr int NS = 2 * C::KSTEPS, NP = C::DBLK, N = NS + NP, L = FA8_LOOKAHEAD;
+    constexpr int NS = C::SB * C::KSTEPS, NP = C::PH * C::DBLK, N = NS + NP, L = FA8_LOOKAHEAD;
     constexpr int NDMA = decltype(load_tag)::value ? 2 * C::DMA_PER_WAVE : 0;
     constexpr int DMA_EVERY = N / (NDMA > 0 ? NDMA : 1);
     const FA_LDS char* kt = (const FA_LDS char*)kbuf;
@@ -240,9 +271,9 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
     auto read = [&](auto I) {
       constexpr int i = decltype(I)::value;
       if constexpr (i < NS)
-        frag[i % (L + 1)] = kfrag(kt, i & 1, i >> 1);
+        frag[i % (L + 1)] = kfrag(kt, i % C::SB, i / C::SB);
       else
-        frag[i % (L + 1)] = vfrag(vt, i - NS);
+        frag[i % (L + 1)] = vfrag(vt + ((i - NS) / C::DBLK) * 64 * C::RB, (i - NS) % C::DBLK);
     };
 #if FA_DEBUG_POISON_LDS
     if constexpr (NDMA > 0) {  // the slots K_(j+1) and V_j are loaded into are retired
@@ -254,27 +285,25 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
       poison_done();
     }
 #endif
-    s0 = f32x16_t{};
-    s1 = f32x16_t{};
+#pragma unroll
+    for (int b = 0; b < C::SB; ++b) sacc[b] = f32x16_t{};
     static_for<L>([&](auto I) { read(I); });
     static_for<N>([&](auto I) {
       constexpr int i = decltype(I)::value;
       if constexpr (i < NS) {
-        if constexpr (i & 1)
-          s1 = mfma8(frag[i % (L + 1)], qf[i >> 1], s1);
-        else
-          s0 = mfma8(frag[i % (L + 1)], qf[i >> 1], s0);
+        sacc[i % C::SB] = mfma8(frag[i % (L + 1)], qf[i / C::SB], sacc[i % C::SB]);
       } else {
-        oacc[i - NS] = mfma8(frag[i % (L + 1)], pb, oacc[i - NS]);
+        constexpr int h = (i - NS) / C::DBLK, mb = (i - NS) % C::DBLK;
+        oacc[mb] = mfma8(frag[i % (L + 1)], pb[h], oacc[mb]);
       }
       if constexpr (i + L < N) read(std::integral_constant<int, i + L>{});
       // the max chain over this phase's S, from the second P V slot on (S is complete by then)
-      constexpr int SPS = (16 + (NP - 2)) / (NP - 1);  // steps per slot over slots NS + 1 .. N - 1
+      constexpr int SPS = (CH + (NP - 2)) / (NP - 1);  // steps per slot over slots NS + 1 .. N - 1
       if constexpr (i >= NS + 1) {
         constexpr int k0 = (i - NS - 1) * SPS;
         static_for<SPS>([&](auto T) {
           constexpr int st = k0 + decltype(T)::value;
-          if constexpr (st < 16) max_step(std::integral_constant<int, st>{});
+          if constexpr (st < CH) max_step(std::integral_constant<int, st>{});
         });
       }
       if constexpr (i == N - 1) smax_pre = max_halves(mxp);
@@ -299,8 +328,9 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int key = tile0 + 8 * (jj >> 2) + 4 * hh + (jj & 3);
-        if (key > lim) s0[jj] = -INFINITY;
-        if (key + 32 > lim) s1[jj] = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < C::SB; ++b)
+          if (key + 32 * b > lim) sacc[b][jj] = -INFINITY;
       }
       row_max_now();
     }
@@ -316,21 +346,25 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
     const float nm = kBias - m2;
     float rs;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const f32x16_t& s = (w < 4) ? s0 : s1;
+    for (int hw = 0; hw < 8 * C::PH; ++hw) {
+      const int h = hw >> 3, w = hw & 7;
+      const f32x16_t& s = sacc[2 * h + (w >= 4 ? 1 : 0)];
       const int j0 = 4 * (w & 3);
       const float p0 = fast_exp2(__builtin_fmaf(s[j0], sl2, nm));
       const float p1 = fast_exp2(__builtin_fmaf(s[j0 + 1], sl2, nm));
       const float p2 = fast_exp2(__builtin_fmaf(s[j0 + 2], sl2, nm));
       const float p3 = fast_exp2(__builtin_fmaf(s[j0 + 3], sl2, nm));
-      rs = w == 0 ? (p0 + p1) + (p2 + p3) : rs + ((p0 + p1) + (p2 + p3));
+      rs = hw == 0 ? (p0 + p1) + (p2 + p3) : rs + ((p0 + p1) + (p2 + p3));
       // the low half is written here and the high half by the next conversion, so the word's old
       // contents (the previous tile's codes, already in the register) need no clearing
-      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb[w], false);
-      pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb[h][w], false);
+      pb[h][w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
     }
     lsum += rs;
-    asm volatile("" : "+v"(pb), "+v"(lsum), "+v"(m2));
+    if constexpr (C::PH == 1)
+      asm volatile("" : "+v"(pb[0]), "+v"(lsum), "+v"(m2));
+    else
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(lsum), "+v"(m2));
   };
 
   auto bar = [&]() {
