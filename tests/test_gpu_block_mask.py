@@ -8,8 +8,10 @@ query block are skipped, partly visible tiles are masked element by element.  Ca
   * rows with no visible key (O = 0 and LSE = -inf exactly), whole 256-row blocks without any
     visible key, and a mask that hides everything;
   * a causal sliding window and packed documents;
-  * the lower-triangle mask, which must give bit for bit what fa_fwd gives with causal = 1 (the
-    same tiles in the same order, the diagonal tiles masked element by element either way);
+  * the lower-triangle mask, which must give bit for bit what fa_fwd gives with causal = 1 at
+    d = 128 (the same 64-key tiles in the same order, the diagonal tiles masked element by element
+    either way); at d = 64 fa_fwd runs 128-key tiles, which group the online softmax differently,
+    so there both are held to the reference instead;
   * the classification pass itself: the per-block tile lists it leaves in the workspace equal a
     classification computed on the host from the boolean mask (integer work: exact);
   * the full-size packed-document workload, every head, as the benchmark times it.
@@ -110,17 +112,21 @@ def test_masked_nothing_visible():
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_triangle_mask_equals_causal_bitwise(d):
+def test_triangle_mask_equals_causal(d):
     w = _w(f"tril_n1000_d{d}", 1, 3, 3, 1000, 1000, d, ("window", 1000))
     allowed = np.tril(np.ones((1000, 1000), bool))
-    _, dev = device_inputs(w)
+    host, dev = device_inputs(w)
     o, lse, _ = _run(w, dev, allowed)
     o2 = torch.empty_like(o)
     l2 = torch.empty_like(lse)
     print("  [fa_fwd] causal, same inputs", flush=True)
     fa.fa_fwd(dev["q"], dev["k"], dev["v"], o2, l2, True, w.scale)
     torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+    if d == 128:
+        assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+    else:
+        _compare(w, host, o, lse, allowed, w.name + " masked")
+        _compare(w, host, o2, l2, allowed, w.name + " causal")
 
 
 def _host_classification(allowed, nq, nk, br=256):
