@@ -106,6 +106,10 @@ constexpr float kLazyRescale = 8.f;
 template <int D, bool MASKED>
 constexpr int kTileKeys = (D == 64 && !MASKED) ? FA_D64_TILE : 64;
 
+#ifndef FA_CAUSAL_SKIP
+#define FA_CAUSAL_SKIP 1  // causal: a wave skips the products and softmax of tiles past its diagonal
+#endif
+
 #ifndef FA_LOOKAHEAD
 #define FA_LOOKAHEAD 8  // MFMAs by which LDS operand reads run ahead
 #endif
@@ -148,6 +152,12 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = wave >> 2;
   const int q_wave0 = qblk * C::BR + wave * 32;  // first query of this wave (wave-uniform)
+  // Causal: the last tile with a key this wave's rows can see.  Every key of a later tile lies past
+  // the diagonal of all its rows: its scores would all be -inf, its P all 0 and its running max
+  // unchanged, so the wave skips the tile's products and softmax (bit for bit the same result)
+  // and only keeps its part of the workgroup's barriers and tile loads.  Fewer products and
+  // exponentials cost less energy, and the kernel is held by the clock the power limit allows.
+  const int j_last = (CAUSAL && FA_CAUSAL_SKIP) ? (q_wave0 + 31 + diag) / C::BC : 0;
 
   // ---- Q^T fragments (B operand) of this block are already in qf: the previous block (or the
   // kernel, for the first one) loaded them.  This block loads the next block's (its own again when
@@ -386,6 +396,18 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
       poison_done();
     }
 #endif
+    if constexpr (CAUSAL && FA_CAUSAL_SKIP) {
+      if (j >= j_last + 2) {  // tiles j - 1 and j lie wholly past this wave's diagonal: loads only
+        static_for<NDMA>([&](auto I) {
+          constexpr int d = decltype(I)::value;
+          if constexpr (d < C::DMA_PER_WAVE)
+            issue_one(Kh, j + 1, kdst, d);
+          else
+            issue_one(Vh, j, vdst, d - C::DMA_PER_WAVE);
+        });
+        return;
+      }
+    }
 #pragma unroll
     for (int b = 0; b < C::SB; ++b) sacc[b] = f32x16_t{};
     static_for<L>([&](auto I) { read(I); });
@@ -433,6 +455,9 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // key's rounding then cancels between O_acc and its normaliser, as if the running max were
   // exact.  LSE keeps the fp32 sum l.
   auto softmax_phase = [&](int j) {
+    if constexpr (CAUSAL && FA_CAUSAL_SKIP) {
+      if (j > j_last) return;  // every score of the tile is masked for this wave: P = 0
+    }
     const int tile0 = tile_of(j) * C::BC;
     uint64_t mcur = 0;
     const bool cut = (tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag);
@@ -566,7 +591,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     softmax_phase(n - 1);  // h = 2n - 1
     wait_loads_but_q();
     bar();
-    pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n
+    if (!(CAUSAL && FA_CAUSAL_SKIP) || n - 1 <= j_last) pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n
     bar();
     bar();  // h = 2n + 1: group 1 finishes
   } else {
@@ -596,7 +621,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     load_q_frags<D>(qf, Q, nbh, Nq, nqblk * C::BR + wave * 32, l32, hh);
     softmax_phase(n - 1);  // h = 2n
     bar();
-    pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n + 1
+    if (!(CAUSAL && FA_CAUSAL_SKIP) || n - 1 <= j_last) pv(((n - 1) & 1) ? vb1 : vb0);  // h = 2n + 1
     bar();
   }
 
