@@ -39,6 +39,9 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 #define FA8_TILE 128  // keys per tile: with 128 the MFMA phase (16 MFMAs at d = 128) is as long as the
                       // bf16 kernel's, and the barriers and per-tile softmax work per key halve
 #endif
+#ifndef FA_CAUSAL_SKIP
+#define FA_CAUSAL_SKIP 1  // causal: a wave skips the products and softmax of tiles past its diagonal
+#endif
 
 template <int D, int BCK = FA8_TILE>
 struct Fp8Cfg {
@@ -118,6 +121,10 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = wave >> 2;
   const int q_wave0 = qblk * C::BR + wave * 32;
+  // Causal: the last tile with a key this wave's rows can see.  Later tiles would give the wave
+  // only -inf scores and P = 0, so it skips their products and softmax (the same result bit for bit)
+  // and keeps only its part of the barriers and tile loads.
+  const int j_last = (CAUSAL && FA_CAUSAL_SKIP) ? (q_wave0 + 31 + diag) / C::BC : 0;
 
   // ---- Q^T fragments (B operand): query l32, dims 64 ks + 32 hh .. + 31
   i32x8_t qf[C::KSTEPS];
@@ -285,6 +292,18 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
       poison_done();
     }
 #endif
+    if constexpr (CAUSAL && FA_CAUSAL_SKIP) {
+      if (j >= j_last + 2) {  // tiles j - 1 and j lie wholly past this wave's diagonal: loads only
+        static_for<NDMA>([&](auto I) {
+          constexpr int d = decltype(I)::value;
+          if constexpr (d < C::DMA_PER_WAVE)
+            issue_one(Kh, j + 1, kdst, d);
+          else
+            issue_one(Vh, j, vdst, d - C::DMA_PER_WAVE);
+        });
+        return;
+      }
+    }
 #pragma unroll
     for (int b = 0; b < C::SB; ++b) sacc[b] = f32x16_t{};
     static_for<L>([&](auto I) { read(I); });
@@ -322,6 +341,9 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
 
   // Softmax phase j: mask, lazy max, P_j = exp2(S_j * sl2 - m + kBias) rounded to E4M3, row sums.
   auto softmax_phase = [&](int j) {
+    if constexpr (CAUSAL && FA_CAUSAL_SKIP) {
+      if (j > j_last) return;  // every score of the tile is masked for this wave: P = 0
+    }
     const int tile0 = tile_of(j) * C::BC;
     if ((tile0 + C::BC > Nk) || (CAUSAL && tile0 + C::BC - 1 > q_wave0 + diag)) {
       const int lim = CAUSAL ? min(Nk - 1, q_wave0 + l32 + diag) : Nk - 1;
@@ -411,7 +433,7 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
     softmax_phase(n - 1);
     wait_loads();
     bar();
-    pv(((n - 1) & 1) ? vb1 : vb0);
+    if (!(CAUSAL && FA_CAUSAL_SKIP) || n - 1 <= j_last) pv(((n - 1) & 1) ? vb1 : vb0);
     bar();
     bar();
   } else {
@@ -440,7 +462,7 @@ __device__ __forceinline__ void fp8_block(const uint8_t* __restrict__ Q, const u
     }
     softmax_phase(n - 1);
     bar();
-    pv(((n - 1) & 1) ? vb1 : vb0);
+    if (!(CAUSAL && FA_CAUSAL_SKIP) || n - 1 <= j_last) pv(((n - 1) & 1) ? vb1 : vb0);
     bar();
   }
 
