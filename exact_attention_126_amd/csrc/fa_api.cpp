@@ -68,9 +68,11 @@ fa_status_t decode_split(const void* q, const void* k, const void* v, void* work
 }
 
 // Masked-forward workspace: tile counts (int32 per query block), tile classes (a byte per block
-// and tile), tile lists (uint16 per block and tile), each part starting on 16 bytes.
+// and tile), tile lists (uint16 per block and tile) and the forward's claim counter (16 bytes), each
+// part starting on 16 bytes.
 int64_t mask_ws_counts_bytes(int64_t n_qblk) { return (4 * n_qblk + 15) / 16 * 16; }
 int64_t mask_ws_cls_bytes(int64_t n_qblk, int64_t nT) { return (n_qblk * nT + 15) / 16 * 16; }
+int64_t mask_ws_lists_bytes(int64_t n_qblk, int64_t nT) { return (2 * n_qblk * nT + 15) / 16 * 16; }
 
 }  // namespace
 
@@ -118,7 +120,7 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, const float*
 size_t fa_fwd_masked_workspace_bytes(int64_t Nq, int64_t Nk) {
   if (Nq <= 0 || Nk <= 0 || Nk > (int64_t)fa::kMaxMaskTiles * 64 || Nq > kI32Max) return 0;
   const int64_t n_qblk = (Nq + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows, nT = (Nk + 63) / 64;
-  return (size_t)(mask_ws_counts_bytes(n_qblk) + mask_ws_cls_bytes(n_qblk, nT) + 2 * n_qblk * nT);
+  return (size_t)(mask_ws_counts_bytes(n_qblk) + mask_ws_cls_bytes(n_qblk, nT) + mask_ws_lists_bytes(n_qblk, nT) + 16);
 }
 
 fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
@@ -146,11 +148,12 @@ fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, void* o, 
   int* counts = reinterpret_cast<int*>(wsb);
   uint8_t* cls = reinterpret_cast<uint8_t*>(wsb + mask_ws_counts_bytes(n_qblk));
   uint16_t* lists = reinterpret_cast<uint16_t*>(wsb + mask_ws_counts_bytes(n_qblk) + mask_ws_cls_bytes(n_qblk, nT));
-  fa::MaskClassifyArgs ca{mask, (int)Nq, (int)Nk, (int)nT, fa::kFwdBlockRows, n_qblk, cls, counts, lists};
+  int* queue = reinterpret_cast<int*>(reinterpret_cast<char*>(lists) + mask_ws_lists_bytes(n_qblk, nT));
+  fa::MaskClassifyArgs ca{mask, (int)Nq, (int)Nk, (int)nT, fa::kFwdBlockRows, n_qblk, cls, counts, lists, queue};
   fa_status_t st = from_hip(fa::launch_mask_classify(ca, stream));
   if (st != FA_OK) return st;
   fa::FwdArgs a{q, k, v, o, lse, (int)B, (int)H, (int)Nq, (int)Nk, (int)d, (int)H_kv, false, 0, scale, num_cus,
-                counts, lists, mask, (int)nT};
+                counts, lists, mask, (int)nT, queue};
   return from_hip(fa::launch_fwd_bf16_masked(a, stream));
 }
 

@@ -89,6 +89,13 @@ struct MaskView {
   const uint64_t* words;
   int nT;        // 64-key tiles per row, ceil(Nk / 64)
   uint16_t* tl;  // LDS, kMaxMaskTiles entries
+  // Dynamic schedule: items (query block, head) in block-major order with the blocks by falling
+  // tile count (order); the next item of the workgroup, claimed before the block by its first
+  // thread (LDS word claim), is read after the block's first barrier into *next_item.
+  const FA_LDS int* order = nullptr;  // kMaxRankedBlocks entries; blocks past them keep their index
+  const FA_LDS int* claim = nullptr;
+  int* next_item = nullptr;
+  int n_items = 0, nbh_all = 0, H = 0, group = 0;
 };
 
 // Lazy rescaling threshold, log2 units: the running max used for the exponentials is only
@@ -96,6 +103,9 @@ struct MaskView {
 // O_acc rescale.  Exponentials are then bounded by 2^kLazyRescale (exact: softmax does not
 // depend on the value subtracted, Day-21 page §5.2).
 constexpr float kLazyRescale = 8.f;
+
+// Query blocks the masked forward ranks by tile count for its schedule (two LDS arrays of ints).
+constexpr int kMaxRankedBlocks = 2048;
 
 #ifndef FA_D64_TILE
 #define FA_D64_TILE 128  // keys per tile of the d = 64 forward without an element mask
@@ -193,10 +203,28 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
   // a partial tile of the mask: some of its keys are visible to some rows of the block
   auto partial = [&](int t) { return MASKED && __builtin_amdgcn_readfirstlane((int)mk.tl[t]) >= 0x8000; };
 
+  // With a mask: the workgroup's next item, published by the barrier before this call site; its
+  // head and query block replace the next-block arguments (used for the Q prefetch).
+  auto take_claim = [&]() {
+    if constexpr (MASKED) {
+      const int nxt = __builtin_amdgcn_readfirstlane(*mk.claim);
+      *mk.next_item = nxt;
+      has_next = nxt < mk.n_items;
+      if (has_next) {
+        nbh = nxt % mk.nbh_all;
+        const int k = nxt / mk.nbh_all;
+        nqblk = k < kMaxRankedBlocks ? __builtin_amdgcn_readfirstlane(mk.order[k]) : k;
+        nkvh = (nbh / mk.H) * (mk.H / mk.group) + (nbh % mk.H) / mk.group;
+      }
+    }
+  };
   if constexpr (MASKED) {
     if (n == 0) {
       // No row of the block sees any key: O = 0 and LSE = ln 0 = -inf.  The next block's Q
-      // fragments are loaded here, as a block with tiles would in its last phase.
+      // fragments are loaded here, as a block with tiles would in its last phase, once the
+      // workgroup's claim of its next item is visible to every wave.
+      __syncthreads();
+      take_claim();
       load_q_frags<D>(qf, Q, nbh, Nq, nqblk * C::BR + wave * 32, l32, hh);
       uint16_t* Oh = O + (int64_t)bh * Nq * D;
       const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -557,6 +585,7 @@ __device__ __forceinline__ bool fwd_block(const uint16_t* __restrict__ Q, const 
     wait_loads();
     bar();
   }
+  if constexpr (MASKED) take_claim();  // a masked block never has its first tile preloaded
   // Slots by tile parity: K_j in kb[j & 1], V_j in vb[j & 1].  Every wave runs 2n + 3 barriers
   // (2n + 2 when the previous block preloaded K_0).
   if (group == 0) {
@@ -681,7 +710,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int n_qblk, int n_items, int items_per_head,
     int xcd_split, float sl2, int H, int group, int diag, int paired, const int* __restrict__ mcounts,
-    const uint16_t* __restrict__ mlists, const uint64_t* __restrict__ mwords, int nT) {
+    const uint16_t* __restrict__ mlists, const uint64_t* __restrict__ mwords, int nT, int* __restrict__ mqueue) {
   using C = Bf16Cfg<D, kTileKeys<D, MASKED>>;
   static_assert(!(CAUSAL && MASKED), "a causal mask is one element mask among others");
   // LDS copy of the current block's tile list (masked forward only)
@@ -712,6 +741,60 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   }
   const int g = blockIdx.x;
+  if constexpr (MASKED) {
+    // The blocks' tile counts differ (by the mask), so the items (query block, head) are handed out
+    // dynamically, heaviest block first: items are block-major over the blocks ranked by falling
+    // tile count, workgroup g starts with item g, and before each block its first thread claims the
+    // next item from the counter (gridDim.x + the count of earlier claims).  The claim alternates
+    // between two LDS words, each read by every wave after the first barrier of the block it was
+    // made for.  Every workgroup ranks the blocks itself, in LDS, from the tile counts; past
+    // kMaxRankedBlocks blocks they keep their index order (still correct, less balanced).
+    __shared__ int s_claim[2];
+    __shared__ int s_cnt[kMaxRankedBlocks], s_order[kMaxRankedBlocks];
+    const int nbh_all = n_items / n_qblk;
+    if (n_qblk <= kMaxRankedBlocks) {
+      for (int q = threadIdx.x; q < n_qblk; q += Bf16Cfg<D>::THREADS) s_cnt[q] = mcounts[q];
+      __syncthreads();
+      for (int q = threadIdx.x; q < n_qblk; q += Bf16Cfg<D>::THREADS) {
+        const int c = s_cnt[q];
+        int rank = 0;
+        for (int p = 0; p < n_qblk; ++p) rank += (s_cnt[p] > c || (s_cnt[p] == c && p < q)) ? 1 : 0;
+        s_order[rank] = q;
+      }
+    } else {
+      for (int q = threadIdx.x; q < kMaxRankedBlocks; q += Bf16Cfg<D>::THREADS) s_order[q] = q;
+    }
+    __syncthreads();
+    const FA_LDS int* order = (const FA_LDS int*)s_order;
+    auto qblk_at = [&](int k) { return k < kMaxRankedBlocks ? __builtin_amdgcn_readfirstlane(order[k]) : k; };
+    int nxt = n_items;
+    MaskView md = mk;
+    md.order = order;
+    md.next_item = &nxt;
+    md.n_items = n_items;
+    md.nbh_all = nbh_all;
+    md.H = H;
+    md.group = group;
+    typename Bf16Cfg<D>::QFrag qf;
+    int item = g, par = 0;
+    if (item < n_items) {
+      const int qb0 = qblk_at(item / nbh_all);
+      load_q_frags<D>(qf.f, Q, item % nbh_all, Nq, qb0 * Bf16Cfg<D>::BR + (threadIdx.x >> 6) * 32, threadIdx.x & 31,
+                      (threadIdx.x >> 5) & 1);
+    }
+    while (item < n_items) {
+      const int bh = item % nbh_all;
+      const int qblk = qblk_at(item / nbh_all);
+      const int kvh = (bh / H) * (H / group) + (bh % H) / group;
+      if (threadIdx.x == 0) s_claim[par] = (int)gridDim.x + atomicAdd(mqueue, 1);
+      md.claim = (const FA_LDS int*)&s_claim[par];
+      fwd_block<D, CAUSAL, MASKED>(Q, K, V, O, LSE, Nq, Nk, sl2, bh, kvh, diag, qblk, n_qblk, kb0, kb1, vb0, vb1, stg,
+                                   qf.f, false, false, bh, kvh, qblk, md);
+      item = nxt;
+      par ^= 1;
+    }
+    return;
+  }
   int it0 = g, it_end = n_items, stride = gridDim.x;
   if (!MASKED && xcd_split) {
     const int per = n_items >> 3;
@@ -719,23 +802,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     it_end = (g & 7) * per + per;
     stride = gridDim.x >> 3;
   }
-  // Item of this workgroup's step r.  With a mask the items are (query block, head) in block-major
-  // order and workgroup g takes position g of every even round of gridDim.x items and position
-  // gridDim.x - 1 - g of every odd one: the blocks' tile counts differ and every workgroup sees
-  // a different block in each round, so the sums even out.
-  auto item_at = [&](int r) {
-    if constexpr (MASKED) return r * (int)gridDim.x + ((r & 1) ? (int)gridDim.x - 1 - g : g);
-    else return it0 + r * stride;
-  };
+  // Item of this workgroup's step r.
+  auto item_at = [&](int r) { return it0 + r * stride; };
   // Block k of item it: its head, K/V head and query block, and the number of blocks of the item.
   auto block_of = [&](int item, int k, int& bh, int& kvh, int& qblk) {
-    if constexpr (MASKED) {
-      const int nbh_all = n_items / n_qblk;
-      bh = item % nbh_all;
-      qblk = item / nbh_all;
-      kvh = (bh / H) * (H / group) + (bh % H) / group;
-      return 1;
-    }
     bh = item / items_per_head;
     const int r = item % items_per_head;
     kvh = (bh / H) * (H / group) + (bh % H) / group;  // K/V head of query head bh
@@ -901,7 +971,8 @@ hipError_t launch_bf16_impl(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MASKED>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.Nq, a.Nk, n_qblk, (int)n_items, items_per_head, xcd_split, a.scale * kLog2e, a.H,
-                     a.H / a.H_kv, a.diag, paired, a.mask_counts, a.mask_lists, a.mask_words, a.mask_tiles);
+                     a.H / a.H_kv, a.diag, paired, a.mask_counts, a.mask_lists, a.mask_words, a.mask_tiles,
+                     a.mask_queue);
   return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@ struct FwdArgs {
   const uint16_t* mask_lists = nullptr;
   const uint64_t* mask_words = nullptr;
   int mask_tiles = 0;  // 64-key tiles per row, ceil(Nk / 64)
+  // the counter from which the workgroups claim (query block, head) items
+  int* mask_queue = nullptr;
 };
 
 struct MaskClassifyArgs {
@@ -41,6 +43,7 @@ struct MaskClassifyArgs {
   uint8_t* cls;     // [n_qblk][nT] class of each tile: 0 empty, 1 full, 2 partial
   int* counts;      // [n_qblk]
   uint16_t* lists;  // [n_qblk][nT]
+  int* queue;       // the forward's claim counter (dynamic item schedule), zeroed by the classification
 };
 
 struct FwdFp8Args {

@@ -14,6 +14,8 @@
 // through LDS and the first writes one class byte per tile: 0 empty, 1 full, 2 partial.
 // mask_compact_kernel: one wave per query block compacts the class bytes into the list, in key
 // order, with a ballot per 64 tiles.
+// The classification also zeroes the counter from which the forward's workgroups claim their
+// (query block, head) items.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -21,8 +23,10 @@ namespace fa {
 namespace {
 
 __global__ __launch_bounds__(256) void mask_classify_kernel(const uint64_t* __restrict__ mask, int Nq, int Nk,
-                                                            int nT, int br, uint8_t* __restrict__ cls) {
+                                                            int nT, int br, uint8_t* __restrict__ cls,
+                                                            int* __restrict__ queue) {
   const int qb = blockIdx.x;
+  if (qb == 0 && blockIdx.y == 0 && threadIdx.x == 0) *queue = 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.y * 64 + lane;
   const int r0 = qb * br, r1 = min(Nq, r0 + br);
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(64) void mask_compact_kernel(const uint8_t* __restr
 
 hipError_t launch_mask_classify(const MaskClassifyArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(mask_classify_kernel, dim3((unsigned)a.n_qblk, (unsigned)((a.nT + 63) / 64)), dim3(256), 0,
-                     stream, a.mask, a.Nq, a.Nk, a.nT, a.br, a.cls);
+                     stream, a.mask, a.Nq, a.Nk, a.nT, a.br, a.cls, a.queue);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mask_compact_kernel, dim3((unsigned)a.n_qblk), dim3(64), 0, stream, a.cls, a.nT, a.counts,

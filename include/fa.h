@@ -122,10 +122,12 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, const float*
  *   words in device memory, shared by every batch and head; bits of keys >= Nk are ignored.  A row
  *   with no visible key gets O = 0 and LSE = -inf.
  *   workspace: caller-owned device memory of at least fa_fwd_masked_workspace_bytes(Nq, Nk)
- *   bytes, 16-byte aligned.  Two small kernels classify every (block of 256 query rows, 64-key
+ *   bytes, 16-byte aligned.  Small kernels classify every (block of 256 query rows, 64-key
  *   tile) of the mask as empty, full or partial and write each block's list of non-empty tiles
- *   there; the forward then streams only those tiles and applies the element mask only on the
- *   partial ones.  The workspace holds nothing across calls.
+ *   there, and a counter from which the forward's workgroups claim (block, head) items, the
+ *   blocks with the most tiles first; the forward then streams only the listed tiles and applies
+ *   the element mask only on the partial ones.  The workspace holds nothing across calls; two
+ *   calls that overlap on one workspace race.
  *   dtype must be FA_DTYPE_BF16; d 64 or 128; Nk <= 131072 (FA_ERR_SHAPE beyond); mask 8-byte
  *   aligned.  Other limits and errors as for fa_fwd_ex.
  */

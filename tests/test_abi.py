@@ -231,8 +231,10 @@ def masked(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=4, H_kv=2, Nq=300, Nk=500, d=128
 
 def test_fwd_masked_validation(L):
     # two 256-row blocks of 8 tiles: counts (2 x 4 bytes, padded to 16), classes (2 x 8 bytes), lists
-    # (2 x 8 x 2 bytes)
-    assert fa.fa_fwd_masked_workspace_bytes(300, 500) == 16 + 16 + 2 * 8 * 2
+    # (2 x 8 x 2 bytes), the forward's claim counter (16 bytes)
+    assert fa.fa_fwd_masked_workspace_bytes(300, 500) == 16 + 16 + 2 * 8 * 2 + 16
+    # 3 blocks of 3 tiles: counts 12 -> 16, classes 9 -> 16, lists 18 -> 32, counter 16
+    assert fa.fa_fwd_masked_workspace_bytes(700, 150) == 16 + 16 + 32 + 16
     assert fa.fa_fwd_masked_workspace_bytes(0, 500) == 0 and fa.fa_fwd_masked_workspace_bytes(10, 131073) == 0
     assert masked(L, mask=0) == 1 and masked(L, ws=0) == 1 and masked(L, q=0) == 1
     assert masked(L, dtype=F32) == 4 and masked(L, d=96) == 4
