@@ -7,6 +7,8 @@
   (the last key tile partial, the diagonal offset 199703).
 * fa_decode_split + fa_decode_combine over 262144 cached keys in 128 splits.
 * fa_bwd for the same kind of chunk against 65537 keys, with grouped heads.
+* fa_fwd_masked with 2048 and 2050 query blocks: the forward ranks up to 2048 blocks by tile count
+  for its schedule, and past that the blocks keep their index order.
 Each case runs at a few heads, so the oracle takes seconds.
 """
 from __future__ import annotations
@@ -124,3 +126,36 @@ def test_bwd_chunk_against_long_cache():
     res = bwd_bounds.reference_and_bounds(f["q"], f["k"], f["v"], f["do"], from_device(o), from_device(lse), w.scale,
                                           w.causal, w.diag)
     bwd_bounds.check({"dq": from_device(dq), "dk": from_device(dk), "dv": from_device(dv)}, res, w.name)
+
+
+def _block_tile_mask(nq, nk, seed, p_empty=0.3, p_full=0.3):
+    """Each (256-row block, 64-key tile) empty, full, or bit by bit at random (seeded); built with
+    broadcasting so that half a million rows take seconds."""
+    g = np.random.default_rng(seed)
+    nqb, nt = -(-nq // 256), -(-nk // 64)
+    cls = g.choice(3, size=(nqb, nt), p=[p_empty, p_full, 1.0 - p_empty - p_full]).astype(np.int8)
+    big = cls[np.arange(nq) // 256][:, np.arange(nk) // 64]
+    bits = g.integers(0, 2, size=(nq, nk), dtype=np.uint8).astype(bool)
+    return (big == 1) | ((big == 2) & bits)
+
+
+@pytest.mark.parametrize("n_blocks", [2048, 2050])
+def test_masked_block_count_at_and_past_the_ranked_limit(n_blocks):
+    """Random empty / full / partial (256-row block, 64-key tile) classes, so the blocks' tile counts
+    differ; 2048 blocks are all ranked for the heaviest-first schedule, 2050 keep index order (the
+    last block ragged).  Every row against the reference."""
+    nq = (n_blocks - 1) * 256 + 77
+    w = Workload(f"masked_{n_blocks}_blocks_nk100_d64", B=1, H=1, H_kv=1, Nq=nq, Nk=100, d=64, dtype="bf16",
+                 causal=False, seed=207)
+    allowed = _block_tile_mask(w.Nq, w.Nk, 208)
+    print(f"  [fa_fwd_masked] {w.name}: Nq={w.Nq} Nk={w.Nk} blocks={n_blocks} visible={masks.visible_pairs(allowed)}",
+          flush=True)
+    host, dev = device_inputs(w)
+    o, lse, _ = _masked_run(w, dev, allowed)
+    f = {x: si.as_f32(w, host[x]) for x in "qkv"}
+    o_ref, l_ref = oracle.attention(f["q"], f["k"], f["v"], w.scale, allowed=allowed)
+    og, lg = from_device(o), from_device(lse)
+    empty = ~allowed.any(axis=1)
+    assert np.all(og[:, :, empty] == 0.0) and np.all(np.isneginf(lg[:, :, empty]))
+    vis = ~empty
+    assert_parity("bf16", metrics(og[:, :, vis], lg[:, :, vis], o_ref[:, :, vis], l_ref[:, :, vis]), w.name)
