@@ -14,7 +14,8 @@ query block are skipped, partly visible tiles are masked element by element.  Ca
     so there both are held to the reference instead;
   * the classification pass itself: the per-block tile lists it leaves in the workspace equal a
     classification computed on the host from the boolean mask (integer work: exact);
-  * the full-size packed-document workload, every head, as the benchmark times it.
+  * the full-size packed-document workload, every head, as the benchmark times it;
+  * bitwise determinism under the dynamic (block, head) schedule.
 Tolerances are the bf16 bars of the forward tests."""
 import numpy as np
 import pytest
@@ -172,3 +173,19 @@ def test_documents_workload_every_head(oracle_pool):
     assert whole["heads"] == w.B * w.H
     assert_parity("bf16", whole, f"{w.name} every head")
     assert_parity("bf16", edges, f"{w.name} edge rows of every head")
+
+
+def test_masked_dynamic_schedule_is_deterministic():
+    """The (block, head) items are claimed dynamically, so which workgroup runs a block changes from
+    run to run; a block's result must not: four runs with four times more items than workgroups
+    give the same bits."""
+    w = _w("docs_b2h64_n2048_det", 2, 64, 16, 2048, 2048, 64, ("documents", 8, 100, 900))
+    allowed = masks.element_mask(w)
+    _, dev = device_inputs(w)
+    runs = []
+    for _ in range(4):
+        o, lse, _ = _run(w, dev, allowed)
+        runs.append((o, lse))
+    for o, lse in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(lse, runs[0][1])
